@@ -1,0 +1,165 @@
+/*
+ * wildcat.h -- C ABI of the WildCat weighted-coreset attention library
+ * (libwildcat.so, HIP for gfx950 / MI355X).
+ *
+ * Method: "WildCat: Near-Linear Attention in Theory and Practice"
+ * (Schroeder & Mackey, arXiv 2602.10056).  Softmax attention
+ * O = diag(A 1)^{-1} A V with A = exp(beta Q K^T) is approximated by attending
+ * over a weighted coreset of r keys:
+ *   wildcat_select  -- RPNys (Alg. 1): randomly pivoted partial Cholesky of
+ *                      H = h_tau(K, K) picks the pivots S and the pivot block L;
+ *   wildcat_weights -- CompressKV (Alg. 2): X = W [V, 1] with
+ *                      W = h_tau(K_S, K_S)^{-1} h_tau(K_S, K), solved through L,
+ *                      plus the column value range of V;
+ *   wildcat_attend  -- WtdAttn (Alg. 3): O_hat = diag(U w)^{-1} U V_S with
+ *                      U = h(Q, K_S), each entry clipped to [v_min j, v_max j].
+ * Calling the three in order on one stream is the WildCat module (Alg. 4).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless a comment says "host".
+ *  - Tensors are dense, row-major, with the head dimension fastest:
+ *      K, V  [batch][kv_heads][n][d]      Q, O  [batch][q_heads][m][d]
+ *    A "unit" is one (batch, kv_head) pair, U = batch * kv_heads; unit
+ *    u = b * kv_heads + h.  Query head h of batch b reads unit
+ *    b * kv_heads + h / (q_heads / kv_heads) (contiguous GQA groups).
+ *  - The caller allocates and owns every buffer, including the workspace
+ *    whose size the *_workspace_bytes queries return.  The library allocates
+ *    no device memory and keeps no state between calls; calls are re-entrant
+ *    as long as concurrent calls use distinct outputs and workspaces.
+ *  - Every call only enqueues kernels on `stream` and returns; results are
+ *    ready when the stream is synchronised.  A status is returned at once for
+ *    argument, shape, dtype and workspace problems; those are checked on the
+ *    host before anything is launched.  WILDCAT_ERR_HIP reports a failed
+ *    launch; faults during execution surface at the caller's next sync.
+ *  - Data conditions are not errors: when the residual trace falls to
+ *    1e-12 of its initial value (or is not finite), or the residual at a
+ *    drawn pivot is not positive, selection stops early with r_eff < r.
+ *    Entries of S past r_eff are -1, rows of L, K_S and X past r_eff are 0
+ *    (such rows contribute nothing to wildcat_attend).
+ *  - Input values must be finite, and beta*<x,y>/tau^2 must stay inside the
+ *    float32 exp range (|.| < 88) for key/key and query/key pairs; the
+ *    library does not rescale.  Larger values give inf/NaN intermediates and
+ *    clipped garbage outputs, not an error status.
+ */
+#ifndef WILDCAT_H
+#define WILDCAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WILDCAT_OK = 0,
+  WILDCAT_ERR_ARG = -1,        /* null pointer, non-finite or non-positive beta/tau */
+  WILDCAT_ERR_DTYPE = -2,      /* dtype not one of wildcat_dtype */
+  WILDCAT_ERR_SHAPE = -3,      /* sizes out of range (see the descriptors) */
+  WILDCAT_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required */
+  WILDCAT_ERR_HIP = -6         /* a kernel launch failed */
+} wildcat_status;
+
+typedef enum { WILDCAT_FP32 = 0, WILDCAT_BF16 = 1 } wildcat_dtype;
+
+/* Keys/values of all units.  Ranges checked by every call:
+ *   batch, kv_heads >= 1;  1 <= n <= 2^24;  d in {16, 32, 64, 128};
+ *   1 <= r <= min(n, 4096);  beta > 0 and tau > 0, both finite;
+ *   recentre in {0, 1};  dtype a wildcat_dtype (of K and V).            */
+typedef struct {
+  int32_t batch, kv_heads, n, d;
+  int32_t r;          /* requested coreset size */
+  double beta;        /* query kernel h(q,k) = exp(beta <q,k>) */
+  double tau;         /* RPNys / weight kernel h_tau(k,k') = exp(beta <k,k'> / tau^2); 1 = h */
+  int32_t recentre;   /* 1: keys minus their per-unit mean for select and weights */
+  int32_t dtype;      /* wildcat_dtype of K and V */
+} wildcat_kv_desc;
+
+/* Queries.  q_heads a positive multiple of kv_heads; 1 <= m <= 2^24; d, r,
+ * beta and dtype as in the kv descriptor used for the compressed cache.   */
+typedef struct {
+  int32_t batch, q_heads, kv_heads, m, d, r;
+  double beta;
+  int32_t dtype;      /* wildcat_dtype of Q and K_S */
+} wildcat_q_desc;
+
+/* Host.  Workspace bytes wildcat_select needs for `desc` (0 on a bad desc). */
+size_t wildcat_select_workspace_bytes(const wildcat_kv_desc* desc);
+
+/* Host.  Workspace bytes wildcat_weights needs for `desc` (0 on a bad desc). */
+size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc);
+
+/*
+ * RPNys pivot selection  [WildCat, RPNys / Alg. 1 paragraph].
+ * Per unit: the residual diagonal starts at h_tau(k_l, k_l); step i draws
+ * s_i = min{ l : C_l > u[i] * T } with C the inclusive prefix sums of the
+ * residual diagonal in index order and T its total (the first index with
+ * positive residual from the end if rounding leaves none), evaluates
+ * g = h_tau(K, k_s) - F[:, :i] F[s, :i]^T, sets column i of the factor to
+ * g / sqrt(g_s), and lowers the residual diagonal by its square (zero at s).
+ * All of this runs in float64, so the draws are reproducible bit for bit.
+ *
+ *   K          [U][n][d] dtype, read only.
+ *   u          [U][r] float64 uniforms in [0, 1): the randomness, supplied by
+ *              the caller (one per step).
+ *   S          [U][r] int32 out: pivots in draw order, -1 past r_eff.
+ *   r_eff      [U] int32 out: number of pivots drawn (<= r).
+ *   L          [U][r][r] float64 out: L[j][k] = F[s_j][k] for k <= j, 0 above
+ *              the diagonal and past r_eff; h_tau(K_S, K_S) = L L^T.
+ *   workspace  >= wildcat_select_workspace_bytes(desc) bytes, 256-byte
+ *              aligned; its contents on entry do not matter.
+ */
+wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K,
+                              const double* u, int32_t* S, int32_t* r_eff,
+                              double* L, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * Nystroem weights and value range  [WildCat, Nystroem paragraph; CompressKV /
+ * Alg. 2 paragraph; Lem. 1 paragraph].
+ * Per unit: Y = h_tau(K_S, K) [V, 1_n] (one exp-kernel contraction, bf16 or
+ * fp32 matrix-core inputs with float32 accumulation), then
+ * X = L^{-T} (L^{-1} Y) in float64 (two triangular solves through the pivot
+ * block), i.e. X = W [V, 1]: V_S = X[:, :d], w = X[:, d].
+ *
+ *   K, V        [U][n][d] dtype, read only.   S, r_eff, L: outputs of select.
+ *   K_S         [U][r][d] dtype out: raw keys K[s_j] (not recentred), 0 rows
+ *               past r_eff.
+ *   X           [U][r][d+1] float32 out, 0 rows past r_eff.
+ *   vmin, vmax  [U][d] float32 out: column minimum / maximum of V over all n.
+ *   workspace   >= wildcat_weights_workspace_bytes(desc) bytes, 256-byte
+ *               aligned; contents on entry do not matter.
+ */
+wildcat_status wildcat_weights(const wildcat_kv_desc* desc, const void* K,
+                               const void* V, const int32_t* S,
+                               const int32_t* r_eff, const double* L, void* K_S,
+                               float* X, float* vmin, float* vmax,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Weighted attention over the compressed cache  [WildCat, plug-in estimator
+ * paragraph; Lem. 1 paragraph; WtdAttn / Alg. 3 paragraph].
+ * Per query row i of query head h (kv unit as above):
+ *   N_i = sum_j exp(beta <q_i, K_S[j]>) X[j, :]       (d+1 numbers)
+ *   O[i][c] = fmin(fmax(N_i[c] / N_i[d], vmin[c]), vmax[c])
+ * Recentring and tau never reach this call: both cancel in the ratio.
+ *
+ *   Q           [batch][q_heads][m][d] dtype, read only.
+ *   K_S, X, vmin, vmax: outputs of wildcat_weights (r rows per unit).
+ *   O           [batch][q_heads][m][d] float32 out.
+ */
+wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q,
+                              const void* K_S, const float* X,
+                              const float* vmin, const float* vmax, float* O,
+                              hipStream_t stream);
+
+/* Host.  Static description of a status code. */
+const char* wildcat_status_string(wildcat_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WILDCAT_H */

@@ -1,0 +1,109 @@
+// C ABI of libwildcat.so: argument validation, workspace sizing, dispatch.
+// The declarations, with the meaning of every argument, are in wildcat.h.
+#include <math.h>
+
+#include "../../include/wildcat.h"
+#include "layout.hpp"
+
+namespace wc {
+hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
+                         const double* u, int32_t* S, int32_t* r_eff, double* L, void* ws, hipStream_t st);
+hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
+                          const void* V, const int32_t* S, const int32_t* r_eff, const double* L, void* K_S,
+                          float* X, float* vmin, float* vmax, void* ws, hipStream_t st);
+hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
+                         const void* K_S, const float* X, const float* vmin, const float* vmax, float* O,
+                         hipStream_t st);
+}  // namespace wc
+
+namespace {
+
+bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wildcat_status check_kv(const wildcat_kv_desc* k) {
+  if (k == nullptr) return WILDCAT_ERR_ARG;
+  if (k->dtype != WILDCAT_FP32 && k->dtype != WILDCAT_BF16) return WILDCAT_ERR_DTYPE;
+  if (!(isfinite(k->beta) && k->beta > 0.0) || !(isfinite(k->tau) && k->tau > 0.0)) return WILDCAT_ERR_ARG;
+  if (k->recentre != 0 && k->recentre != 1) return WILDCAT_ERR_ARG;
+  if (k->batch < 1 || k->kv_heads < 1 || k->n < 1 || k->n > wc::kMaxN || !valid_d(k->d)) return WILDCAT_ERR_SHAPE;
+  if (k->r < 1 || k->r > k->n || k->r > wc::kMaxR) return WILDCAT_ERR_SHAPE;
+  if ((int64_t)k->batch * k->kv_heads > 65535) return WILDCAT_ERR_SHAPE;
+  return WILDCAT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wildcat_select_workspace_bytes(const wildcat_kv_desc* desc) {
+  if (check_kv(desc) != WILDCAT_OK) return 0;
+  return wc::SelectLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r).total;
+}
+
+size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc) {
+  if (check_kv(desc) != WILDCAT_OK) return 0;
+  return wc::WeightsLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r).total;
+}
+
+wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K, const double* u, int32_t* S,
+                              int32_t* r_eff, double* L, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  wildcat_status st = check_kv(desc);
+  if (st != WILDCAT_OK) return st;
+  if (!K || !u || !S || !r_eff || !L || !aligned16(K)) return WILDCAT_ERR_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < wildcat_select_workspace_bytes(desc))
+    return WILDCAT_ERR_WORKSPACE;
+  const int U = desc->batch * desc->kv_heads;
+  const double c = desc->beta / (desc->tau * desc->tau);
+  hipError_t e = wc::launch_select(desc->dtype == WILDCAT_BF16, U, desc->n, desc->d, desc->r, c, desc->recentre,
+                                   K, u, S, r_eff, L, workspace, stream);
+  return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
+}
+
+wildcat_status wildcat_weights(const wildcat_kv_desc* desc, const void* K, const void* V, const int32_t* S,
+                               const int32_t* r_eff, const double* L, void* K_S, float* X, float* vmin,
+                               float* vmax, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  wildcat_status st = check_kv(desc);
+  if (st != WILDCAT_OK) return st;
+  if (!K || !V || !S || !r_eff || !L || !K_S || !X || !vmin || !vmax) return WILDCAT_ERR_ARG;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(K_S)) return WILDCAT_ERR_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < wildcat_weights_workspace_bytes(desc))
+    return WILDCAT_ERR_WORKSPACE;
+  const int U = desc->batch * desc->kv_heads;
+  const double c = desc->beta / (desc->tau * desc->tau);
+  hipError_t e = wc::launch_weights(desc->dtype == WILDCAT_BF16, U, desc->n, desc->d, desc->r, c, desc->recentre,
+                                    K, V, S, r_eff, L, K_S, X, vmin, vmax, workspace, stream);
+  return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
+}
+
+wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q, const void* K_S, const float* X,
+                              const float* vmin, const float* vmax, float* O, hipStream_t stream) {
+  if (desc == nullptr) return WILDCAT_ERR_ARG;
+  if (desc->dtype != WILDCAT_FP32 && desc->dtype != WILDCAT_BF16) return WILDCAT_ERR_DTYPE;
+  if (!(isfinite(desc->beta) && desc->beta > 0.0)) return WILDCAT_ERR_ARG;
+  if (desc->batch < 1 || desc->kv_heads < 1 || desc->q_heads < 1 || desc->q_heads % desc->kv_heads != 0 ||
+      desc->m < 1 || desc->m > (1 << 24) || !valid_d(desc->d) || desc->r < 1 || desc->r > wc::kMaxR ||
+      (int64_t)desc->batch * desc->q_heads > 65535)
+    return WILDCAT_ERR_SHAPE;
+  if (!Q || !K_S || !X || !vmin || !vmax || !O || !aligned16(Q) || !aligned16(K_S)) return WILDCAT_ERR_ARG;
+  const int Uq = desc->batch * desc->q_heads;
+  const int group = desc->q_heads / desc->kv_heads;
+  hipError_t e = wc::launch_attend(desc->dtype == WILDCAT_BF16, Uq, group, desc->m, desc->d, desc->r, desc->beta,
+                                   Q, K_S, X, vmin, vmax, O, stream);
+  return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
+}
+
+const char* wildcat_status_string(wildcat_status status) {
+  switch (status) {
+    case WILDCAT_OK: return "ok";
+    case WILDCAT_ERR_ARG: return "invalid argument (null or misaligned pointer, bad beta/tau/recentre)";
+    case WILDCAT_ERR_DTYPE: return "unsupported dtype";
+    case WILDCAT_ERR_SHAPE: return "shape out of range";
+    case WILDCAT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case WILDCAT_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,514 @@
+// Exp-kernel contractions of WildCat on gfx950 matrix cores.
+//
+//   weights (CompressKV):  Y[a, :] = sum_b exp(c <k_a, k_b> + rowc_a + colc_b) [V_b, 1]
+//   attend  (WtdAttn):     N[i, :] = sum_j exp(beta <q_i, ks_j>) X_j,  O = clip(N[:, :d] / N[:, d])
+//
+// [WildCat (arXiv 2602.10056): plug-in estimator paragraph (W [V, 1] is formed
+// before the queries are applied), Lem. 1 paragraph (clip to the column value
+// range), CompressKV / Alg. 2 and WtdAttn / Alg. 3 paragraphs.]
+//
+// Both are one kernel template: a workgroup of 4 waves owns 64 rows of the
+// left operand (16 per wave, fragments kept in registers) and streams the right
+// operand in tiles of 64 rows through LDS.  Per 32 right rows a wave issues
+//   scores^T (16 rows x 16 cols) x2 : v_mfma_f32_16x16x32_bf16 over d
+//   P = exp2(...) in fp32, rounded to bf16 in registers
+//   P x [V] (16 x d)                : v_mfma_f32_16x16x32_bf16 over the 32 rows
+// The score tiles are computed transposed with a row permutation chosen so
+// that every lane ends up holding 8 consecutive right rows of its own left row,
+// which is exactly the A-operand layout of the second MFMA: P never leaves the
+// registers.  V is staged transposed in LDS so the second MFMA's B operand is
+// one 16-byte LDS read.  The last column ([.., 1] or w) is accumulated on the
+// vector ALU from the same bf16-rounded P.  No running maximum is needed: the
+// exponents are bounded by the input-range contract.
+#include "common.hpp"
+#include "layout.hpp"
+
+namespace wc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct ContractArgs {
+  const void* A;        // left rows  [units][rowsA][D] (bf16 or fp32)
+  const void* B;        // right rows [unitsB][rowsB][D]
+  const void* Vs;       // values: V [unitsB][rowsB][D] (weights) or X [unitsB][rowsB][D+1] fp32 (attend)
+  const float* rowc;    // [units][rowsA] exponent offsets (weights + recentring) or null
+  const float* colc;    // [unitsB][rowsB] exponent offsets (weights + recentring) or null
+  float* out;           // weights: ypart [nsplit][units][rowsA][D+1]; attend: O [units][rowsA][D]
+  const float* vmin;    // attend: [unitsB][D]
+  const float* vmax;
+  int rowsA, rowsB;
+  int chunk;            // right rows per split (weights); rowsB for attend
+  int group;            // left unit u reads right unit u / group (GQA); 1 for weights
+  int units;
+  float scale;          // c (weights) or beta (attend)
+};
+
+enum { kModeWeights = 0, kModeAttend = 1 };
+
+// Physical LDS row of right row `k` inside its 32-row block: the rows one
+// score MFMA reads (lanes 0..15) become 16 consecutive LDS rows.
+__device__ __forceinline__ int perm_row(int k) {
+  const int blk = k & ~31, w = k & 31;
+  const int a = w >> 3, t = (w >> 2) & 1, i = w & 3;
+  return blk + 16 * t + 4 * a + i;
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kBlock) void expmm_bf16(ContractArgs p) {
+  constexpr int KP = D + 8;          // LDS row pitch of the right tile (bf16)
+  constexpr int VP = kTileKeys + 8;  // LDS row pitch of the transposed values (bf16)
+  constexpr int DK = D < 32 ? 1 : D / 32;
+  constexpr int CT = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kTileKeys * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sVT[D * VP];
+  __shared__ float sE[kTileKeys];
+  __shared__ float sC[kTileKeys];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int unit = blockIdx.z;
+  const int unitB = unit / p.group;
+  const int a0 = blockIdx.y * kTileRows;
+  const int split = blockIdx.x;
+  const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
+  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (size_t)unit * p.rowsA * D;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (size_t)unitB * p.rowsB * D;
+
+  // Left-row fragments: lane holds row a0 + 16*wave + r16, k = 32*dk + 8*g .. +7.
+  const int arow = a0 + wave * 16 + r16;
+  bf16x8 afrag[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    const int k0 = 32 * dk + 8 * g;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (arow < p.rowsA && k0 < D) v = *reinterpret_cast<const uint4*>(A + (size_t)arow * D + k0);
+    afrag[dk] = __builtin_bit_cast(bf16x8, v);
+  }
+  float rc2 = 0.0f;
+  if (MODE == kModeWeights && p.rowc != nullptr && arow < p.rowsA) rc2 = p.rowc[(size_t)unit * p.rowsA + arow] * kLog2e;
+  const float sc2 = p.scale * kLog2e;
+
+  f32x4 oacc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float eacc = 0.0f;
+
+  for (int b0 = b_begin; b0 < b_end; b0 += kTileKeys) {
+    // ---- stage the right tile (permuted rows) and the transposed values
+    for (int q = t; q < kTileKeys * (D / 8); q += kBlock) {
+      const int row = q / (D / 8), c8 = q % (D / 8);
+      const int b = b0 + row;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (b < b_end) v = *reinterpret_cast<const uint4*>(B + (size_t)b * D + 8 * c8);
+      *reinterpret_cast<uint4*>(&sB[perm_row(row) * KP + 8 * c8]) = v;
+    }
+    for (int q = t; q < (kTileKeys / 2) * (D / 8); q += kBlock) {
+      const int rp = q % (kTileKeys / 2), c8 = q / (kTileKeys / 2);
+      const int b = b0 + 2 * rp;
+      uint32_t lo[8], hi[8];
+      if (MODE == kModeWeights) {
+        const uint16_t* V = reinterpret_cast<const uint16_t*>(p.Vs) + (size_t)unitB * p.rowsB * D;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u), y = make_uint4(0u, 0u, 0u, 0u);
+        if (b < b_end) x = *reinterpret_cast<const uint4*>(V + (size_t)b * D + 8 * c8);
+        if (b + 1 < b_end) y = *reinterpret_cast<const uint4*>(V + (size_t)(b + 1) * D + 8 * c8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo[2 * j] = xs[j] & 0xFFFFu; lo[2 * j + 1] = xs[j] >> 16;
+          hi[2 * j] = ys[j] & 0xFFFFu; hi[2 * j + 1] = ys[j] >> 16;
+        }
+      } else {
+        const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = b < b_end ? X[(size_t)b * (D + 1) + 8 * c8 + j] : 0.0f;
+          const float y = b + 1 < b_end ? X[(size_t)(b + 1) * (D + 1) + 8 * c8 + j] : 0.0f;
+          lo[j] = __builtin_bit_cast(uint16_t, (__bf16)x);
+          hi[j] = __builtin_bit_cast(uint16_t, (__bf16)y);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint32_t*>(&sVT[(8 * c8 + j) * VP + 2 * rp]) = lo[j] | (hi[j] << 16);
+    }
+    if (t < kTileKeys) {
+      const int b = b0 + t;
+      if (MODE == kModeAttend) {
+        const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
+        sE[t] = b < b_end ? X[(size_t)b * (D + 1) + D] : 0.0f;
+      } else {
+        sE[t] = b < b_end ? 1.0f : 0.0f;
+        sC[t] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // ---- two 32-row blocks per tile
+#pragma unroll
+    for (int kb = 0; kb < kTileKeys / 32; ++kb) {
+      float pv[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+          const int k0 = 32 * dk + 8 * g;
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (k0 < D) v = *reinterpret_cast<const uint4*>(&sB[(32 * kb + 16 * tt + r16) * KP + k0]);
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), afrag[dk], s4, 0, 0, 0);
+        }
+        // s4[i] = score of left row r16 with right row 32kb + 8g + 4tt + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = 32 * kb + 8 * g + 4 * tt + i;
+          float arg = fmaf(s4[i], sc2, rc2);
+          if (MODE == kModeWeights) arg += sC[kk];
+          pv[4 * tt + i] = sE[kk] != 0.0f || MODE == kModeAttend ? exp2f(arg) : 0.0f;
+        }
+      }
+      // bf16 P as the A operand of the value MFMA; extra column on the VALU.
+      bf16x8 pfrag;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const __bf16 h = (__bf16)pv[j];
+        pfrag[j] = h;
+        const int kk = 32 * kb + 8 * g + j;
+        eacc = fmaf((float)h, sE[kk], eacc);
+      }
+      if (MODE == kModeAttend) {
+        // right rows past rowsB were staged as zeros; mask their P out
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b0 + 32 * kb + 8 * g + j >= b_end) pfrag[j] = (__bf16)0.0f;
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sVT[(16 * ct + r16) * VP + 32 * kb + 8 * g]);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfrag, __builtin_bit_cast(bf16x8, v), oacc[ct], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // eacc: partial over this lane's 8-row groups -> full sum for left row r16.
+  eacc += __shfl_xor(eacc, 16, 64);
+  eacc += __shfl_xor(eacc, 32, 64);
+
+  // oacc[ct][i] = result for left row 16*wave + 4g + i, column 16ct + r16.
+  if (MODE == kModeWeights) {
+    float* Y = p.out + ((size_t)split * p.units + unit) * p.rowsA * (D + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = a0 + wave * 16 + 4 * g + i;
+      if (row < p.rowsA) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[(size_t)row * (D + 1) + 16 * ct + r16] = oacc[ct][i];
+      }
+    }
+    if (g == 0 && arow < p.rowsA) Y[(size_t)arow * (D + 1) + D] = eacc;
+  } else {
+    float* O = p.out + (size_t)unit * p.rowsA * D;
+    const float* vmn = p.vmin + (size_t)unitB * D;
+    const float* vmx = p.vmax + (size_t)unitB * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 4 * g + i;
+      const float e = __shfl(eacc, rl, 64);
+      const int row = a0 + wave * 16 + rl;
+      if (row < p.rowsA) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c = 16 * ct + r16;
+          const float x = oacc[ct][i] / e;
+          O[(size_t)row * D + c] = fminf(fmaxf(x, vmn[c]), vmx[c]);
+        }
+      }
+    }
+  }
+}
+
+// fp32 inputs: the same contraction on the vector ALU in fp32 (P is not
+// rounded).  A workgroup owns 64 left rows; thread (row, quarter) accumulates
+// every fourth output column of its row.
+template <int D, int MODE>
+__global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
+  __shared__ float sB[kTileKeys][D + 1];
+  __shared__ float sV[kTileKeys][D + 1];
+  __shared__ float sE[kTileKeys];
+  __shared__ float sC[kTileKeys];
+  const int t = threadIdx.x, rl = t >> 2, qc = t & 3;
+  const int unit = blockIdx.z, unitB = unit / p.group;
+  const int a0 = blockIdx.y * kTileRows, split = blockIdx.x;
+  const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
+  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  const float* A = reinterpret_cast<const float*>(p.A) + (size_t)unit * p.rowsA * D;
+  const float* B = reinterpret_cast<const float*>(p.B) + (size_t)unitB * p.rowsB * D;
+  const int row = a0 + rl;
+  float arow[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) arow[c] = row < p.rowsA ? A[(size_t)row * D + c] : 0.0f;
+  const float rc = (MODE == kModeWeights && p.rowc != nullptr && row < p.rowsA) ? p.rowc[(size_t)unit * p.rowsA + row] : 0.0f;
+  constexpr int NC = (D + 4) / 4;   // columns 0..D (D+1 of them), strided by 4
+  float acc[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) acc[j] = 0.0f;
+  for (int b0 = b_begin; b0 < b_end; b0 += kTileKeys) {
+    for (int q = t; q < kTileKeys * D; q += kBlock) {
+      const int rr = q / D, c = q % D, b = b0 + rr;
+      sB[rr][c] = b < b_end ? B[(size_t)b * D + c] : 0.0f;
+      float v = 0.0f;
+      if (b < b_end) {
+        v = MODE == kModeWeights ? reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * D + c]
+                                 : reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * (D + 1) + c];
+      }
+      sV[rr][c] = v;
+    }
+    if (t < kTileKeys) {
+      const int b = b0 + t;
+      if (MODE == kModeWeights) {
+        sV[t][D] = b < b_end ? 1.0f : 0.0f;
+        sC[t] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] : 0.0f;
+      } else {
+        sV[t][D] = b < b_end ? reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * (D + 1) + D] : 0.0f;
+        sC[t] = 0.0f;
+      }
+      sE[t] = b < b_end ? 1.0f : 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < kTileKeys; ++k) {
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) s = fmaf(arow[c], sB[k][c], s);
+      const float pk = sE[k] != 0.0f ? expf(fmaf(s, p.scale, rc + sC[k])) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = qc + 4 * j;
+        if (c <= D) acc[j] = fmaf(pk, sV[k][c], acc[j]);
+      }
+    }
+    __syncthreads();
+  }
+  if (MODE == kModeWeights) {
+    if (row < p.rowsA) {
+      float* Y = p.out + (((size_t)split * p.units + unit) * p.rowsA + row) * (D + 1);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = qc + 4 * j;
+        if (c <= D) Y[c] = acc[j];
+      }
+    }
+  } else {
+    // the normaliser (column D) sits in the thread with qc == D % 4
+    __shared__ float sN[kTileRows];
+    if (qc == (D & 3)) sN[rl] = acc[D / 4];
+    __syncthreads();
+    if (row < p.rowsA) {
+      const float e = sN[rl];
+      float* O = p.out + ((size_t)unit * p.rowsA + row) * D;
+      const float* vmn = p.vmin + (size_t)unitB * D;
+      const float* vmx = p.vmax + (size_t)unitB * D;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = qc + 4 * j;
+        if (c < D) O[c] = fminf(fmaxf(acc[j] / e, vmn[c]), vmx[c]);
+      }
+    }
+  }
+}
+
+// K_S[u][j] = K[u][S[u][j]] for j < r_eff, zero rows after; optional per-pivot
+// exponent offsets for recentring: rowc = c (|kbar|^2 - <k_s, kbar>).
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void gather_pivots(const TK* K, const int32_t* S, const int32_t* r_eff,
+                                                        TK* K_S, const double* kbar, float* rowc,
+                                                        int n, int r, double c) {
+  __shared__ double red[kBlock];
+  const int u = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const bool live = j < r_eff[u];
+  const int s = live ? S[(size_t)u * r + j] : 0;
+  for (int e = t; e < D; e += kBlock) {
+    TK x;
+    if (live) x = K[((size_t)u * n + s) * D + e];
+    else memset(&x, 0, sizeof(TK));
+    K_S[((size_t)u * r + j) * D + e] = x;
+  }
+  if (rowc != nullptr) {
+    double acc = 0.0;
+    for (int e = t; e < D; e += kBlock) {
+      const double kb = kbar[(size_t)u * D + e];
+      const double x = live ? (double)Elem<TK>::f32(K, ((size_t)u * n + s) * D + e) : 0.0;
+      acc += kb * kb - x * kb;
+    }
+    red[t] = acc;
+    __syncthreads();
+    if (t == 0) {
+      double sum = 0.0;
+      for (int q = 0; q < kBlock; ++q) sum += red[q];
+      rowc[(size_t)u * r + j] = live ? (float)(c * sum) : 0.0f;
+    }
+  }
+}
+
+// Per-key exponent offsets for recentring: colc = -c <kbar, k_l>.
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void key_offsets(const TK* K, const double* kbar, float* colc, int n, double c) {
+  const int u = blockIdx.y;
+  const int l = blockIdx.x * kBlock + threadIdx.x;
+  if (l >= n) return;
+  double acc = 0.0;
+  for (int e = 0; e < D; ++e) acc = fma((double)Elem<TK>::f32(K, ((size_t)u * n + l) * D + e), kbar[(size_t)u * D + e], acc);
+  colc[(size_t)u * n + l] = (float)(-c * acc);
+}
+
+// Per-unit key mean in fp64 (recentring).
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void key_mean(const TK* K, double* kbar, int n) {
+  __shared__ double part[kBlock];
+  const int u = blockIdx.x, t = threadIdx.x;
+  constexpr int PH = kBlock / D;
+  const int c = t % D, ph = t / D;
+  double acc = 0.0;
+  for (int l = ph; l < n; l += PH) acc += (double)Elem<TK>::f32(K, ((size_t)u * n + l) * D + c);
+  part[t] = acc;
+  __syncthreads();
+  if (t < D) {
+    double s = 0.0;
+    for (int q = 0; q < PH; ++q) s += part[q * D + t];
+    kbar[(size_t)u * D + t] = s / (double)n;
+  }
+}
+
+// Column min / max of V: partials over kMinMaxRows rows, then a reduction.
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, float* part, int n, int nmm) {
+  __shared__ float smn[kBlock], smx[kBlock];
+  const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+  constexpr int PH = kBlock / D;
+  const int c = t % D, ph = t / D;
+  const int l0 = blk * kMinMaxRows, l1 = min(n, l0 + kMinMaxRows);
+  float mn = INFINITY, mx = -INFINITY;
+  for (int l = l0 + ph; l < l1; l += PH) {
+    const float x = Elem<TK>::f32(V, ((size_t)u * n + l) * D + c);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  smn[t] = mn;
+  smx[t] = mx;
+  __syncthreads();
+  if (t < D) {
+    for (int q = 1; q < PH; ++q) { mn = fminf(mn, smn[q * D + t]); mx = fmaxf(mx, smx[q * D + t]); }
+    float* o = part + (((size_t)u * nmm + blk) * 2) * D;
+    o[t] = mn;
+    o[D + t] = mx;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void value_range_final(const float* part, float* vmin, float* vmax, int d, int nmm, int U) {
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= U * d) return;
+  const int u = e / d, c = e % d;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int b = 0; b < nmm; ++b) {
+    const float* o = part + (((size_t)u * nmm + b) * 2) * d;
+    mn = fminf(mn, o[c]);
+    mx = fmaxf(mx, o[d + c]);
+  }
+  vmin[e] = mn;
+  vmax[e] = mx;
+}
+
+// ---------------------------------------------------------------- host side
+template <int D, int MODE>
+static void launch_expmm(bool bf16, const ContractArgs& a, dim3 grid, hipStream_t st) {
+  if (bf16) expmm_bf16<D, MODE><<<grid, kBlock, 0, st>>>(a);
+  else expmm_f32<D, MODE><<<grid, kBlock, 0, st>>>(a);
+}
+
+template <int MODE>
+static hipError_t launch_expmm_d(bool bf16, int d, const ContractArgs& a, dim3 grid, hipStream_t st) {
+  switch (d) {
+    case 16: launch_expmm<16, MODE>(bf16, a, grid, st); break;
+    case 32: launch_expmm<32, MODE>(bf16, a, grid, st); break;
+    case 64: launch_expmm<64, MODE>(bf16, a, grid, st); break;
+    case 128: launch_expmm<128, MODE>(bf16, a, grid, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename TK, int D>
+static void launch_weights_prep(int U, int n, int r, double c, int recentre, const void* K, const void* V,
+                                const int32_t* S, const int32_t* r_eff, void* K_S, const WeightsLayout& lay,
+                                char* w, float* vmin, float* vmax, hipStream_t st) {
+  const TK* Kt = reinterpret_cast<const TK*>(K);
+  double* kbar = reinterpret_cast<double*>(w + lay.kbar);
+  float* rowc = reinterpret_cast<float*>(w + lay.rowc);
+  float* colc = reinterpret_cast<float*>(w + lay.colc);
+  if (recentre) {
+    key_mean<TK, D><<<U, kBlock, 0, st>>>(Kt, kbar, n);
+    key_offsets<TK, D><<<dim3((n + kBlock - 1) / kBlock, U), kBlock, 0, st>>>(Kt, kbar, colc, n, c);
+  }
+  gather_pivots<TK, D><<<dim3(r, U), kBlock, 0, st>>>(Kt, S, r_eff, reinterpret_cast<TK*>(K_S), kbar,
+                                                       recentre ? rowc : nullptr, n, r, c);
+  float* mm = reinterpret_cast<float*>(w + lay.mmpart);
+  value_range_part<TK, D><<<dim3(lay.nmm, U), kBlock, 0, st>>>(reinterpret_cast<const TK*>(V), mm, n, lay.nmm);
+  value_range_final<<<(U * D + kBlock - 1) / kBlock, kBlock, 0, st>>>(mm, vmin, vmax, D, lay.nmm, U);
+}
+
+template <typename TK>
+static hipError_t launch_prep_d(int d, int U, int n, int r, double c, int recentre, const void* K, const void* V,
+                                const int32_t* S, const int32_t* r_eff, void* K_S, const WeightsLayout& lay,
+                                char* w, float* vmin, float* vmax, hipStream_t st) {
+  switch (d) {
+    case 16: launch_weights_prep<TK, 16>(U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st); break;
+    case 32: launch_weights_prep<TK, 32>(U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st); break;
+    case 64: launch_weights_prep<TK, 64>(U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st); break;
+    case 128: launch_weights_prep<TK, 128>(U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L,
+                       const int32_t* r_eff, float* X, hipStream_t st);
+
+// CompressKV after selection: K_S, value range, Y = h_tau(K_S, K) [V, 1], X.
+hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
+                          const void* V, const int32_t* S, const int32_t* r_eff, const double* L, void* K_S,
+                          float* X, float* vmin, float* vmax, void* ws, hipStream_t st) {
+  const WeightsLayout lay(U, n, d, r);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = bf16 ? launch_prep_d<bf16_t>(d, U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st)
+                      : launch_prep_d<float>(d, U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st);
+  if (e != hipSuccess) return e;
+  ContractArgs a{};
+  a.A = K_S; a.B = K; a.Vs = V;
+  a.rowc = recentre ? reinterpret_cast<const float*>(w + lay.rowc) : nullptr;
+  a.colc = recentre ? reinterpret_cast<const float*>(w + lay.colc) : nullptr;
+  a.out = reinterpret_cast<float*>(w + lay.ypart);
+  a.rowsA = r; a.rowsB = n; a.chunk = lay.sp.chunk; a.group = 1; a.units = U;
+  a.scale = (float)c;
+  const dim3 grid(lay.sp.nsplit, lay.sp.tiles_a, U);
+  e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, grid, st);
+  if (e != hipSuccess) return e;
+  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, r_eff, X, st);
+}
+
+// WtdAttn: O = clip(h(Q, K_S) X / (h(Q, K_S) w)).
+hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
+                         const void* K_S, const float* X, const float* vmin, const float* vmax, float* O,
+                         hipStream_t st) {
+  ContractArgs a{};
+  a.A = Q; a.B = K_S; a.Vs = X; a.out = O; a.vmin = vmin; a.vmax = vmax;
+  a.rowsA = m; a.rowsB = r; a.chunk = r; a.group = group; a.units = Uq;
+  a.scale = (float)beta;
+  const dim3 grid(1, (m + kTileRows - 1) / kTileRows, Uq);
+  return launch_expmm_d<kModeAttend>(bf16 != 0, d, a, grid, st);
+}
+
+}  // namespace wc

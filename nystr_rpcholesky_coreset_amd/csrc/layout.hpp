@@ -1,0 +1,84 @@
+// Workspace layouts and launch geometry of the WildCat library (host side).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wc {
+
+constexpr int kSelRowsPerThread = 2;                        // fp64 rows per lane in the step kernel
+constexpr int kSelRowsPerBlock = 256 * kSelRowsPerThread;   // rows of one workgroup = one scan block
+constexpr int kMaxR = 4096;
+constexpr int kMaxN = 1 << 21;
+
+inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// RPNys workspace for U units of n keys, rank r, head dim d.
+//   F      [U][r][npad] fp64   factor, row i = column i of the Cholesky factor
+//   dres   [U][npad]    fp64   residual diagonal (0 on padding rows)
+//   bsum   [U][nb]      fp64   per-workgroup residual sums of the last step
+//   pivbuf [U][2][pbs]  fp64   next pivot: s, sqrt(g_s), F[s,:i], k_s (double buffered by step parity)
+//   T0     [U]          fp64   initial residual trace
+//   kbar   [U][d]       fp64   key mean (recentring only)
+//   stopped, reff, counter [U] int32 / int32 / uint32
+struct SelectLayout {
+  int nb, npad, pbs;
+  size_t F, dres, bsum, pivbuf, T0, kbar, stopped, reff, counter, total;
+  SelectLayout(int U, int n, int d, int r) {
+    nb = (n + kSelRowsPerBlock - 1) / kSelRowsPerBlock;
+    npad = nb * kSelRowsPerBlock;
+    pbs = (2 + r + d + 3) / 4 * 4;
+    size_t o = 0;
+    F = o;       o += al256((size_t)U * r * npad * 8);
+    dres = o;    o += al256((size_t)U * npad * 8);
+    bsum = o;    o += al256((size_t)U * nb * 8);
+    pivbuf = o;  o += al256((size_t)U * 2 * pbs * 8);
+    T0 = o;      o += al256((size_t)U * 8);
+    kbar = o;    o += al256((size_t)U * d * 8);
+    stopped = o; o += al256((size_t)U * 4);
+    reff = o;    o += al256((size_t)U * 4);
+    counter = o; o += al256((size_t)U * 4);
+    total = o;
+  }
+};
+
+// Geometry of the exp-kernel contraction Y = h_tau(K_S, K) [V, 1].
+constexpr int kTileRows = 64;   // A rows (pivot keys or queries) per workgroup
+constexpr int kTileKeys = 64;   // B rows (keys or pivots) staged per iteration
+
+struct ContractSplit {
+  int tiles_a, nsplit, chunk;   // chunk: keys per split, multiple of kTileKeys
+  ContractSplit(int U, int r, int n) {
+    tiles_a = (r + kTileRows - 1) / kTileRows;
+    int want = (2048 + tiles_a * U - 1) / (tiles_a * U);
+    int maxs = (n + kTileKeys - 1) / kTileKeys;
+    nsplit = want < 1 ? 1 : (want > maxs ? maxs : want);
+    chunk = ((n + nsplit - 1) / nsplit + kTileKeys - 1) / kTileKeys * kTileKeys;
+    nsplit = (n + chunk - 1) / chunk;
+  }
+};
+
+// Weights workspace:
+//   ypart   [nsplit][U][r][d+1] fp32   split-n partial contractions
+//   mmpart  [U][nmm][2][d]      fp32   partial column min / max of V
+//   kbar    [U][d]              fp64   key mean (recentring only)
+//   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
+//   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
+constexpr int kMinMaxRows = 1024;   // rows of V per min/max partial
+struct WeightsLayout {
+  ContractSplit sp;
+  int nmm;
+  size_t ypart, mmpart, kbar, rowc, colc, total;
+  WeightsLayout(int U, int n, int d, int r) : sp(U, r, n) {
+    nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
+    size_t o = 0;
+    ypart = o;  o += al256((size_t)sp.nsplit * U * r * (d + 1) * 4);
+    mmpart = o; o += al256((size_t)U * nmm * 2 * d * 4);
+    kbar = o;   o += al256((size_t)U * d * 8);
+    rowc = o;   o += al256((size_t)U * r * 4);
+    colc = o;   o += al256((size_t)U * n * 4);
+    total = o;
+  }
+};
+
+}  // namespace wc

@@ -1,0 +1,168 @@
+"""Thin ctypes binding over libwildcat.so (C ABI in include/wildcat.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the computation runs in the HIP library.  If the
+library has not been built this module raises at import -- there is no
+fallback path.
+
+Shapes (row-major, head dim fastest):
+    K, V   [batch][kv_heads][n][d]       Q, O   [batch][q_heads][m][d]
+    u      [batch*kv_heads][r] float64   S      [batch*kv_heads][r] int32
+    L      [batch*kv_heads][r][r] float64
+    K_S    [batch][kv_heads][r][d]       X      [batch][kv_heads][r][d+1] float32
+    vmin, vmax [batch][kv_heads][d] float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwildcat.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nystr_rpcholesky_coreset_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+WILDCAT_OK = 0
+WILDCAT_ERR_ARG = -1
+WILDCAT_ERR_DTYPE = -2
+WILDCAT_ERR_SHAPE = -3
+WILDCAT_ERR_WORKSPACE = -4
+WILDCAT_ERR_HIP = -6
+WILDCAT_FP32 = 0
+WILDCAT_BF16 = 1
+
+EXPORTED = (
+    "wildcat_select_workspace_bytes", "wildcat_weights_workspace_bytes", "wildcat_select",
+    "wildcat_weights", "wildcat_attend", "wildcat_status_string",
+)
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("beta", ctypes.c_double),
+                ("tau", ctypes.c_double), ("recentre", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class QDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("d", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("beta", ctypes.c_double), ("dtype", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+lib.wildcat_select_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+lib.wildcat_select_workspace_bytes.restype = ctypes.c_size_t
+lib.wildcat_weights_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+lib.wildcat_weights_workspace_bytes.restype = ctypes.c_size_t
+lib.wildcat_select.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+lib.wildcat_select.restype = ctypes.c_int
+lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]
+lib.wildcat_weights.restype = ctypes.c_int
+lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.wildcat_attend.restype = ctypes.c_int
+lib.wildcat_status_string.argtypes = [ctypes.c_int]
+lib.wildcat_status_string.restype = ctypes.c_char_p
+
+
+class WildcatError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.wildcat_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != WILDCAT_OK:
+        raise WildcatError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return WILDCAT_BF16
+    if t.dtype == torch.float32:
+        return WILDCAT_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kv_desc(K: torch.Tensor, r: int, beta: float, tau: float = 1.0, recentre: bool = False) -> KVDesc:
+    B, H, n, d = K.shape
+    return KVDesc(B, H, n, d, int(r), float(beta), float(tau), int(bool(recentre)), _dtype_code(K))
+
+
+def select_workspace_bytes(desc: KVDesc) -> int:
+    return lib.wildcat_select_workspace_bytes(ctypes.byref(desc))
+
+
+def weights_workspace_bytes(desc: KVDesc) -> int:
+    return lib.wildcat_weights_workspace_bytes(ctypes.byref(desc))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def select(K, u, r, beta, tau=1.0, recentre=False, workspace=None, stream=None):
+    """wildcat_select: returns (S [U][r] int32, r_eff [U] int32, L [U][r][r] float64)."""
+    desc = kv_desc(K, r, beta, tau, recentre)
+    U = desc.batch * desc.kv_heads
+    dev = K.device
+    S = torch.empty((U, r), dtype=torch.int32, device=dev)
+    r_eff = torch.empty((U,), dtype=torch.int32, device=dev)
+    L = torch.empty((U, r, r), dtype=torch.float64, device=dev)
+    nbytes = select_workspace_bytes(desc)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.wildcat_select(ctypes.byref(desc), _ptr(K), _ptr(u), _ptr(S), _ptr(r_eff), _ptr(L),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "wildcat_select")
+    return S, r_eff, L
+
+
+def weights(K, V, S, r_eff, L, r, beta, tau=1.0, recentre=False, workspace=None, stream=None):
+    """wildcat_weights: returns (K_S, X, vmin, vmax)."""
+    desc = kv_desc(K, r, beta, tau, recentre)
+    B, H, n, d = K.shape
+    dev = K.device
+    K_S = torch.empty((B, H, r, d), dtype=K.dtype, device=dev)
+    X = torch.empty((B, H, r, d + 1), dtype=torch.float32, device=dev)
+    vmin = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    vmax = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    nbytes = weights_workspace_bytes(desc)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.wildcat_weights(ctypes.byref(desc), _ptr(K), _ptr(V), _ptr(S), _ptr(r_eff), _ptr(L), _ptr(K_S),
+                               _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)), "wildcat_weights")
+    return K_S, X, vmin, vmax
+
+
+def attend(Q, K_S, X, vmin, vmax, beta, stream=None, out=None):
+    """wildcat_attend: returns O [batch][q_heads][m][d] float32."""
+    B, Hq, m, d = Q.shape
+    Hkv, r = K_S.shape[1], K_S.shape[2]
+    desc = QDesc(B, Hq, Hkv, m, d, r, float(beta), _dtype_code(Q))
+    O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
+    _check(lib.wildcat_attend(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(O),
+                              _stream(stream)), "wildcat_attend")
+    return O
+
+
+def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None):
+    """WildCat module: select -> weights -> attend on one stream.  Returns (O, parts)."""
+    S, r_eff, L = select(K, u, r, beta, tau, recentre, stream=stream)
+    K_S, X, vmin, vmax = weights(K, V, S, r_eff, L, r, beta, tau, recentre, stream=stream)
+    O = attend(Q, K_S, X, vmin, vmax, beta, stream=stream)
+    return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)

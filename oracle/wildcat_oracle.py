@@ -80,7 +80,8 @@ def draw_pivot(dres, u):
     drawn).  If rounding leaves no such l, the last index with positive
     residual is taken.
 
-    Returns (s, T, margin) with margin = min_l |C_l - u T| / T.
+    Returns (s, T, gap) with gap = min_l |C_l - u T| (a diagnostic: how far
+    the draw is from flipping to a neighbouring index).
     """
     C = np.cumsum(dres)
     T = C[-1]
@@ -90,8 +91,8 @@ def draw_pivot(dres, u):
         s = int(hits[0])
     else:
         s = int(np.flatnonzero(dres > 0)[-1])
-    margin = float(np.min(np.abs(C - target)) / T) if T > 0 else 0.0
-    return s, T, margin
+    gap = float(np.min(np.abs(C - target)))
+    return s, T, gap
 
 
 @dataclass
@@ -102,7 +103,7 @@ class SelectResult:
     F: np.ndarray            # r_eff x n partial Cholesky factor (row i = column i of the factor)
     dres: np.ndarray         # residual diagonal after the last step
     T0: float
-    margins: list = field(default_factory=list)
+    margins: list = field(default_factory=list)   # per draw: gap / T0 (see draw_pivot)
     kernel_evals: int = 0    # number of h_tau entries evaluated
 
 
@@ -138,7 +139,7 @@ def rpnys_select(K, u, r, beta, tau=1.0, recentre=False):
         T = np.cumsum(dres)[-1]
         if not (T > STOP_REL * T0):
             break
-        s, T, margin = draw_pivot(dres, u[i])
+        s, T, gap = draw_pivot(dres, u[i])
         g = selection_kernel(Kc, Kc[s:s + 1], beta, tau)[:, 0] - F[:i].T @ F[:i, s]
         evals += n
         if not (g[s] > 0):
@@ -147,7 +148,7 @@ def rpnys_select(K, u, r, beta, tau=1.0, recentre=False):
         dres = np.maximum(dres - F[i] ** 2, 0.0)
         dres[s] = 0.0
         S.append(s)
-        margins.append(margin)
+        margins.append(gap / T0)
     r_eff = len(S)
     S = np.asarray(S, dtype=np.int64)
     L = np.tril(F[:r_eff][:, S].T)

@@ -1,0 +1,158 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Oracle-sized cases compare every output element by element; they span several
+workgroups of the selection kernel (512 keys each) with ragged tails, several
+64-row contraction tiles, GQA groups, recentring and tau != 1.  Pivots must
+match bit for bit (a mismatch is tolerated only at an fp64 near tie, see
+_helpers.check_pivots), L to 1e-9 of its scale, the value range exactly, and
+O within 2e-3 (fp32) or 2e-2 (bf16) of max|V|.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from nystr_rpcholesky_coreset_amd import inputs as I
+from oracle import wildcat_oracle as orc
+
+from _helpers import check_pivots, oracle_attend_rows, oracle_units, rel_max, to_device, tol_for
+
+pytestmark = pytest.mark.gpu
+
+W = I.WORKLOADS
+C1, C2, C3, C4, C5 = (W[k] for k in I.WORKLOAD_ORDER)
+
+SMALL_CASES = {
+    "probe_full": C1,
+    "probe_ragged": I.scaled_workload(C1, n=1000, m=333, r=77, seed=7),
+    "vit_b3": I.scaled_workload(C2, batch=3),
+    "latent_h2": I.scaled_workload(C3, batch=1, q_heads=2, kv_heads=2),
+    "kv_gqa8x2_ragged": I.scaled_workload(C4, q_heads=8, kv_heads=2, n=5000, r=200),
+    "sphere_h2": I.scaled_workload(C5, q_heads=2, kv_heads=2, n=3000, m=700, r=150),
+    "kv_recentre_tau": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=1500, r=100, recentre=True, tau=1.7),
+    "probe_recentre": I.scaled_workload(C1, n=700, m=100, r=40, recentre=True, tau=0.8, seed=9),
+}
+
+
+def _run_gpu(inp):
+    import torch
+    from nystr_rpcholesky_coreset_amd import wildcat as wc
+    w = inp["workload"]
+    Q = to_device(inp["Q"], w.dtype)
+    K = to_device(inp["K"], w.dtype)
+    V = to_device(inp["V"], w.dtype)
+    u = torch.from_numpy(inp["u"]).cuda()
+    O, parts = wc.forward(Q, K, V, u, w.r, w.beta, w.tau, w.recentre)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in parts.items()}
+    out["O"] = O.cpu()
+    for k in ("K_S",):
+        out[k] = out[k].float() if out[k].dtype == torch.bfloat16 else out[k]
+    return {k: v.numpy() for k, v in out.items()}
+
+
+def _compare_unit(inp, g, u, ures, qrows=None, check_O=True):
+    w = inp["workload"]
+    sel = ures.sel
+    matched = check_pivots(g["S"][u], int(g["r_eff"][u]), sel)
+    full = matched == sel.r_eff
+    re = matched
+    L = g["L"][u]
+    scale = max(1.0, float(np.abs(sel.L).max()))
+    assert rel_max(L[:re, :re], sel.L[:re, :re], scale) < 1e-9
+    assert np.all(L[:re][np.triu_indices(re, 1)] == 0.0)
+    b, h = divmod(u, w.kv_heads)
+    vmin, vmax = g["vmin"][b, h], g["vmax"][b, h]
+    np.testing.assert_array_equal(vmin, ures.vmin.astype(np.float32))
+    np.testing.assert_array_equal(vmax, ures.vmax.astype(np.float32))
+    KS = g["K_S"][b, h]
+    np.testing.assert_array_equal(KS[:re], ures.K_S[:re].astype(np.float32))
+    if full:
+        assert np.all(L[sel.r_eff:] == 0.0) and np.all(KS[sel.r_eff:] == 0) and np.all(g["X"][b, h][sel.r_eff:] == 0)
+    if not (check_O and full):
+        return
+    Vmax = float(np.abs(I.to_f64(inp["V"], w.dtype)).max())
+    group = w.q_heads // w.kv_heads
+    for hq in range(h * group, (h + 1) * group):
+        qu = b * w.q_heads + hq
+        Oo = oracle_attend_rows(inp, ures, qu, qrows)
+        Og = g["O"][b, hq] if qrows is None else g["O"][b, hq][qrows]
+        err = rel_max(Og, Oo, Vmax)
+        print(f"unit {u} q-head {hq}: max|dO|/max|V| = {err:.3e}")
+        assert err < tol_for(w.dtype), err
+        assert np.all(Og >= vmin[None, :]) and np.all(Og <= vmax[None, :])
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_parity_small(name):
+    w = SMALL_CASES[name]
+    print(f"case {name}: {w}", flush=True)
+    inp = I.make_inputs(w)
+    g = _run_gpu(inp)
+    units = list(range(w.units))
+    ref = oracle_units(inp, units)
+    for u in units:
+        _compare_unit(inp, g, u, ref[u])
+
+
+def _edge_inputs(K, V, Q, r, beta, dtype="fp32"):
+    w = I.Workload("edge", "unit_ball", 1, Q.shape[0], 1, Q.shape[1], K.shape[0], K.shape[1], r, beta, dtype, 0)
+    store = (lambda x: x.astype(np.float32)) if dtype == "fp32" else (lambda x: I.bf16_bits_from_f32(x.astype(np.float32)))
+    return {"Q": store(Q)[None], "K": store(K)[None, None], "V": store(V)[None, None],
+            "u": np.random.default_rng(5).random((1, r)), "workload": w}
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_keys_stop_after_one_pivot(dtype):
+    rng = np.random.default_rng(1)
+    K = np.zeros((300, 32))
+    V = rng.standard_normal((300, 32))
+    Q = rng.standard_normal((2, 50, 32)) / 6
+    inp = _edge_inputs(K, V, Q, 16, 0.2, dtype)
+    g = _run_gpu(inp)
+    assert g["r_eff"][0] == 1
+    assert np.all(g["S"][0][1:] == -1)
+    Vd = I.to_f64(inp["V"], dtype)[0, 0]
+    np.testing.assert_allclose(g["O"][0], np.broadcast_to(Vd.mean(0), (2, 50, 32)), atol=tol_for(dtype) * np.abs(Vd).max())
+
+
+def test_duplicated_keys_stop_at_distinct_count():
+    rng = np.random.default_rng(2)
+    base = rng.standard_normal((6, 16)) / 2
+    K = base[rng.integers(0, 6, 900)]
+    K[:6] = base
+    V = rng.standard_normal((900, 16))
+    Q = rng.standard_normal((1, 64, 16)) / 2
+    inp = _edge_inputs(K, V, Q, 20, 0.5)
+    g = _run_gpu(inp)
+    ref = oracle_units(inp, [0])[0]
+    assert ref.sel.r_eff == 6
+    _compare_unit(inp, g, 0, ref)
+    exact = orc.exact_attention(Q[0], K, V, 0.5)
+    assert rel_max(g["O"][0, 0], exact, np.abs(V).max()) < 2e-3
+
+
+@pytest.mark.parametrize("n,r", [(64, 64), (1, 1), (513, 1), (600, 600)])
+def test_rank_extremes(n, r):
+    """Well-conditioned kernels (|k|^2 ~ 16, beta 1/2) so that r = n runs to
+    full rank; r = n must then reproduce exact softmax."""
+    rng = np.random.default_rng(n + r)
+    K = rng.standard_normal((n, 16))
+    V = rng.standard_normal((n, 16))
+    Q = rng.standard_normal((1, 40, 16)) / 2
+    inp = _edge_inputs(K, V, Q, r, 0.5)
+    g = _run_gpu(inp)
+    ref = oracle_units(inp, [0])[0]
+    _compare_unit(inp, g, 0, ref)
+    if r == n:
+        assert ref.sel.r_eff == n
+        exact = orc.exact_attention(Q[0], K, V, 0.5)
+        assert rel_max(g["O"][0, 0], exact, np.abs(V).max()) < 2e-3
+
+
+def test_repeat_calls_are_bitwise_deterministic():
+    w = SMALL_CASES["kv_gqa8x2_ragged"]
+    inp = I.make_inputs(w)
+    a, b = _run_gpu(inp), _run_gpu(inp)
+    for k in ("S", "r_eff", "L", "X", "O"):
+        np.testing.assert_array_equal(a[k], b[k])
