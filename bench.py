@@ -1,0 +1,229 @@
+"""Throughput of the WildCat hot path on one MI355X.
+
+One step = wildcat_select + wildcat_weights + wildcat_attend over the whole
+synthetic workload (inputs already resident in HBM).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+Default workload: KV-cache compression with GQA, 32 query heads over 8 kv
+heads, n = 32768 keys, d = 128, r = 1024 pivots per kv head, 64 queries per
+query head, bf16 inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "kvcache_gqa32x8_n32768_d128_r1024_bf16"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
+MFMA_FP32_TFLOPS = 157.3
+
+
+def select_bytes(w, e):
+    """Algorithmic HBM bytes of RPNys over all units: per unit and round i the
+    keys (n*d*e), the new factor column (8n), the residual diagonal read and
+    write (16n) and the previous factor columns (8*n*i)."""
+    U, n, d, r = w.units, w.n, w.d, w.r
+    return U * n * (r * (d * e + 24) + 4 * r * (r - 1))
+
+
+def contraction_flops(w):
+    """Matrix-core flops: scores and value products of both contractions."""
+    c1 = w.units * (2 * w.r * w.n * w.d + 2 * w.r * w.n * (w.d + 1))
+    c2 = w.q_units * (2 * w.m * w.r * w.d + 2 * w.m * w.r * (w.d + 1))
+    return c1, c2
+
+
+def cpu_baseline(w, inp, target_s=20.0):
+    """The oracle as it stands, timed on host cores on a bounded sample: whole
+    kv units (select + weights + attend for their query heads), as many as fit
+    in about target_s seconds (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from nystr_rpcholesky_coreset_amd import inputs as I
+    from oracle import wildcat_oracle as orc
+
+    K = I.to_f64(inp["K"], w.dtype)
+    V = I.to_f64(inp["V"], w.dtype)
+    Qa = inp["Q"]
+    group = w.q_heads // w.kv_heads
+    rows = 0
+    t0 = time.perf_counter()
+    units_done = 0
+    for uidx in range(w.units):
+        b, h = divmod(uidx, w.kv_heads)
+        ur = orc.compress_unit(K[b, h], V[b, h], inp["u"][uidx], w.r, w.beta, w.tau, w.recentre)
+        for hq in range(h * group, (h + 1) * group):
+            Q = I.to_f64(Qa[b, hq], w.dtype)
+            orc.plugin_attend(Q, ur.K_S, ur.X, ur.vmin, ur.vmax, w.beta)
+            rows += Q.shape[0]
+        units_done += 1
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": rows / dt, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{units_done} of {w.units} kv units ({rows} query rows), full n={w.n}, r={w.r}; "
+                      f"{dt:.1f} s on {threads} BLAS threads (os.cpu_count()={os.cpu_count()})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(units would shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from nystr_rpcholesky_coreset_amd import inputs as I
+    from nystr_rpcholesky_coreset_amd import wildcat as wc
+
+    w = I.WORKLOADS[args.workload]
+    e = 2 if w.dtype == "bf16" else 4
+    inp = I.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    Q, K, V = to_dev(inp["Q"]), to_dev(inp["K"]), to_dev(inp["V"])
+    u = torch.from_numpy(inp["u"]).to(dev)
+    desc = wc.kv_desc(K, w.r, w.beta, w.tau, w.recentre)
+    ws_sel = torch.empty(wc.select_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(wc.weights_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        S, r_eff, L = wc.select(K, u, w.r, w.beta, w.tau, w.recentre, workspace=ws_sel)
+        if ev:
+            ev[1].record(stream)
+        K_S, X, vmin, vmax = wc.weights(K, V, S, r_eff, L, w.r, w.beta, w.tau, w.recentre, workspace=ws_w)
+        if ev:
+            ev[2].record(stream)
+        O = wc.attend(Q, K_S, X, vmin, vmax, w.beta)
+        if ev:
+            ev[3].record(stream)
+        return O, r_eff
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        O, r_eff = step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(3)] for k in range(args.steps)])
+    t_sel, t_wts, t_att = (float(np.median(ph[:, j])) for j in range(3))
+    ms_step = wall * 1000.0 / args.steps
+    reff = r_eff.cpu().numpy()
+    assert np.all(reff == w.r), f"early stop on the bench workload: r_eff {reff}"
+    assert torch.isfinite(O).all().item()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # exact softmax attention on the same GPU (comparator only)
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    grp = w.q_heads // w.kv_heads
+    Ke = K.repeat_interleave(grp, dim=1).contiguous()
+    Ve = V.repeat_interleave(grp, dim=1).contiguous()
+    exact = {}
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION),
+                     ("math", SDPBackend.MATH)):
+        try:
+            with sdpa_kernel([be]):
+                torch.nn.functional.scaled_dot_product_attention(Q, Ke, Ve, scale=w.beta)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    torch.nn.functional.scaled_dot_product_attention(Q, Ke, Ve, scale=w.beta)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                exact = {"backend": name, "ms": e0.elapsed_time(e1) / 5}
+                break
+        except RuntimeError:
+            continue
+    del Ke, Ve
+
+    sb = select_bytes(w, e)
+    per_launch_bytes = sb / w.r
+    avg_launch_ms = t_sel / w.r
+    achieved = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    c1, c2 = contraction_flops(w)
+    rows = w.query_rows
+    value = rows / (ms_step * 1e-3)
+    line = {
+        "metric": "WildCat attention query rows/sec at n=32k,r=1k; RPCholesky ms; %HBM/%MFMA peak",
+        "value": value,
+        "unit": "query rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64+bf16" if w.dtype == "bf16" else "f64+fp32",
+        "data": "synthetic (seeded; shapes and statistics of a GQA KV-cache workload)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "n": w.n, "m": w.m, "d": w.d, "r": w.r, "beta": w.beta, "input_dtype": w.dtype},
+        "phases_ms": {"select": t_sel, "weights": t_wts, "attend": t_att},
+        "rpcholesky_ms": t_sel,
+        "select_hbm_frac": sb / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "contraction_gflop": {"weights": c1 / 1e9, "attend": c2 / 1e9},
+        "attend_only_rows_per_s": rows / (t_att * 1e-3),
+        "exact_attention_gpu": exact,
+        "roofline": {
+            "kernel": "rpc_step (one RPNys round, all units)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": per_launch_bytes,
+            "avg_launch_ms": avg_launch_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
