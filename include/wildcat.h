@@ -64,9 +64,11 @@ typedef enum {
 typedef enum { WILDCAT_FP32 = 0, WILDCAT_BF16 = 1 } wildcat_dtype;
 
 /* Keys/values of all units.  Ranges checked by every call:
- *   batch, kv_heads >= 1;  1 <= n <= 2^24;  d in {16, 32, 64, 128};
- *   1 <= r <= min(n, 4096);  beta > 0 and tau > 0, both finite;
- *   recentre in {0, 1};  dtype a wildcat_dtype (of K and V).            */
+ *   batch, kv_heads >= 1 and batch * kv_heads <= 65535;  1 <= n <= 2^21;
+ *   d in {16, 32, 64, 128};  1 <= r <= min(n, 4096);  beta > 0 and tau > 0,
+ *   both finite;  recentre in {0, 1};  dtype a wildcat_dtype (of K and V).
+ * K, V, Q, K_S and the workspaces must be 16-byte aligned (WILDCAT_ERR_ARG,
+ * or WILDCAT_ERR_WORKSPACE for a workspace, otherwise).                  */
 typedef struct {
   int32_t batch, kv_heads, n, d;
   int32_t r;          /* requested coreset size */
@@ -76,8 +78,9 @@ typedef struct {
   int32_t dtype;      /* wildcat_dtype of K and V */
 } wildcat_kv_desc;
 
-/* Queries.  q_heads a positive multiple of kv_heads; 1 <= m <= 2^24; d, r,
- * beta and dtype as in the kv descriptor used for the compressed cache.   */
+/* Queries.  q_heads a positive multiple of kv_heads, batch * q_heads <=
+ * 65535; 1 <= m <= 2^24; d, r (<= 4096), beta and dtype as in the kv
+ * descriptor used for the compressed cache.                               */
 typedef struct {
   int32_t batch, q_heads, kv_heads, m, d, r;
   double beta;
@@ -107,7 +110,7 @@ size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc);
  *   r_eff      [U] int32 out: number of pivots drawn (<= r).
  *   L          [U][r][r] float64 out: L[j][k] = F[s_j][k] for k <= j, 0 above
  *              the diagonal and past r_eff; h_tau(K_S, K_S) = L L^T.
- *   workspace  >= wildcat_select_workspace_bytes(desc) bytes, 256-byte
+ *   workspace  >= wildcat_select_workspace_bytes(desc) bytes, 16-byte
  *              aligned; its contents on entry do not matter.
  */
 wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K,
@@ -128,7 +131,7 @@ wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K,
  *               past r_eff.
  *   X           [U][r][d+1] float32 out, 0 rows past r_eff.
  *   vmin, vmax  [U][d] float32 out: column minimum / maximum of V over all n.
- *   workspace   >= wildcat_weights_workspace_bytes(desc) bytes, 256-byte
+ *   workspace   >= wildcat_weights_workspace_bytes(desc) bytes, 16-byte
  *               aligned; contents on entry do not matter.
  */
 wildcat_status wildcat_weights(const wildcat_kv_desc* desc, const void* K,

@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/wildcat.h declares, sizes workspaces, and rejects bad arguments on
+the host before anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wildcat.h")
+
+wc = pytest.importorskip("nystr_rpcholesky_coreset_amd.wildcat", reason="libwildcat.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wildcat_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_path_calls():
+    names = _declared()
+    for n in ("wildcat_select", "wildcat_weights", "wildcat_attend"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert set(names) == set(wc.EXPORTED)
+    for n in names:
+        assert hasattr(wc.lib, n), n
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+
+
+def _kv(**kw):
+    base = dict(batch=2, kv_heads=4, n=5000, d=128, r=256, beta=0.1, tau=1.0, recentre=0, dtype=wc.WILDCAT_BF16)
+    base.update(kw)
+    return wc.KVDesc(*[base[f] for f, _ in wc.KVDesc._fields_])
+
+
+def test_workspace_sizes_are_positive_and_grow_with_r():
+    a = wc.select_workspace_bytes(_kv(r=128))
+    b = wc.select_workspace_bytes(_kv(r=256))
+    assert 0 < a < b
+    # the factor dominates: U * r * npad * 8 bytes
+    assert b >= 8 * 256 * 5120 * 8
+    assert wc.weights_workspace_bytes(_kv()) > 0
+    assert wc.select_workspace_bytes(_kv(d=100)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=100), wc.WILDCAT_ERR_SHAPE),
+    (dict(r=0), wc.WILDCAT_ERR_SHAPE),
+    (dict(r=5001), wc.WILDCAT_ERR_SHAPE),
+    (dict(n=5000, r=4097), wc.WILDCAT_ERR_SHAPE),
+    (dict(n=0, r=1), wc.WILDCAT_ERR_SHAPE),
+    (dict(batch=0), wc.WILDCAT_ERR_SHAPE),
+    (dict(dtype=7), wc.WILDCAT_ERR_DTYPE),
+    (dict(beta=0.0), wc.WILDCAT_ERR_ARG),
+    (dict(beta=float("nan")), wc.WILDCAT_ERR_ARG),
+    (dict(tau=-1.0), wc.WILDCAT_ERR_ARG),
+    (dict(tau=float("inf")), wc.WILDCAT_ERR_ARG),
+    (dict(recentre=2), wc.WILDCAT_ERR_ARG),
+])
+def test_select_rejects_bad_descriptors(kw, status):
+    d = _kv(**kw)
+    assert wc.lib.wildcat_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == status
+    assert wc.lib.wildcat_weights(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, 1 << 40, None) == status
+
+
+def test_null_and_misaligned_pointers_and_small_workspace():
+    d = _kv()
+    assert wc.lib.wildcat_select(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == wc.WILDCAT_ERR_ARG
+    assert wc.lib.wildcat_select(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == wc.WILDCAT_ERR_ARG
+    assert wc.lib.wildcat_select(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None) == wc.WILDCAT_ERR_ARG
+    need = wc.select_workspace_bytes(d)
+    assert wc.lib.wildcat_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == wc.WILDCAT_ERR_WORKSPACE
+    assert wc.lib.wildcat_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == wc.WILDCAT_ERR_WORKSPACE
+    needw = wc.weights_workspace_bytes(d)
+    assert wc.lib.wildcat_weights(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  needw - 1, None) == wc.WILDCAT_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_heads=6, kv_heads=4), wc.WILDCAT_ERR_SHAPE),
+    (dict(d=48), wc.WILDCAT_ERR_SHAPE),
+    (dict(m=0), wc.WILDCAT_ERR_SHAPE),
+    (dict(r=5000), wc.WILDCAT_ERR_SHAPE),
+    (dict(beta=-1.0), wc.WILDCAT_ERR_ARG),
+    (dict(dtype=3), wc.WILDCAT_ERR_DTYPE),
+])
+def test_attend_rejects_bad_descriptors(kw, status):
+    base = dict(batch=1, q_heads=8, kv_heads=4, m=64, d=128, r=256, beta=0.1, dtype=wc.WILDCAT_BF16)
+    base.update(kw)
+    q = wc.QDesc(*[base[f] for f, _ in wc.QDesc._fields_])
+    assert wc.lib.wildcat_attend(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -6):
+        assert wc.lib.wildcat_status_string(s)
