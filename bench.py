@@ -209,7 +209,7 @@ def main():
         "attend_only_rows_per_s": rows / (t_att * 1e-3),
         "exact_attention_gpu": exact,
         "roofline": {
-            "kernel": "rpc_step (one RPNys round, all units)",
+            "kernel": "one RPNys round over all units: rpc_step (factor/diagonal stream) + rpc_draw (next pivot)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -7,8 +7,8 @@
 // before the queries are applied), Lem. 1 paragraph (clip to the column value
 // range), CompressKV / Alg. 2 and WtdAttn / Alg. 3 paragraphs.]
 //
-// Both are one kernel template: a workgroup of 4 waves owns 64 rows of the
-// left operand (16 per wave, fragments kept in registers) and streams the right
+// Both are one kernel template: a workgroup of NW waves owns 16 rows of the
+// left operand per wave (fragments kept in registers) and streams the right
 // operand in tiles of 64 rows through LDS.  Per 32 right rows a wave issues
 //   scores^T (16 rows x 16 cols) x2 : v_mfma_f32_16x16x32_bf16 over d
 //   P = exp2(...) in fp32, rounded to bf16 in registers
@@ -56,8 +56,9 @@ __device__ __forceinline__ int perm_row(int k) {
   return blk + 16 * t + 4 * a + i;
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kBlock) void expmm_bf16(ContractArgs p) {
+template <int D, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
+  constexpr int NTH = 64 * NW;       // threads; the workgroup owns 16 * NW left rows
   constexpr int KP = D + 8;          // LDS row pitch of the right tile (bf16)
   constexpr int VP = kTileKeys + 8;  // LDS row pitch of the transposed values (bf16)
   constexpr int DK = D < 32 ? 1 : D / 32;
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void expmm_bf16(ContractArgs p) {
   const int g = lane >> 4, r16 = lane & 15;
   const int unit = blockIdx.z;
   const int unitB = unit / p.group;
-  const int a0 = blockIdx.y * kTileRows;
+  const int a0 = blockIdx.y * 16 * NW;
   const int split = blockIdx.x;
   const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
   const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
@@ -100,14 +101,14 @@ __global__ __launch_bounds__(kBlock) void expmm_bf16(ContractArgs p) {
 
   for (int b0 = b_begin; b0 < b_end; b0 += kTileKeys) {
     // ---- stage the right tile (permuted rows) and the transposed values
-    for (int q = t; q < kTileKeys * (D / 8); q += kBlock) {
+    for (int q = t; q < kTileKeys * (D / 8); q += NTH) {
       const int row = q / (D / 8), c8 = q % (D / 8);
       const int b = b0 + row;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (b < b_end) v = *reinterpret_cast<const uint4*>(B + (size_t)b * D + 8 * c8);
       *reinterpret_cast<uint4*>(&sB[perm_row(row) * KP + 8 * c8]) = v;
     }
-    for (int q = t; q < (kTileKeys / 2) * (D / 8); q += kBlock) {
+    for (int q = t; q < (kTileKeys / 2) * (D / 8); q += NTH) {
       const int rp = q % (kTileKeys / 2), c8 = q / (kTileKeys / 2);
       const int b = b0 + 2 * rp;
       uint32_t lo[8], hi[8];
@@ -136,14 +137,14 @@ __global__ __launch_bounds__(kBlock) void expmm_bf16(ContractArgs p) {
       for (int j = 0; j < 8; ++j)
         *reinterpret_cast<uint32_t*>(&sVT[(8 * c8 + j) * VP + 2 * rp]) = lo[j] | (hi[j] << 16);
     }
-    if (t < kTileKeys) {
-      const int b = b0 + t;
+    for (int q = t; q < kTileKeys; q += NTH) {
+      const int b = b0 + q;
       if (MODE == kModeAttend) {
         const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
-        sE[t] = b < b_end ? X[(size_t)b * (D + 1) + D] : 0.0f;
+        sE[q] = b < b_end ? X[(size_t)b * (D + 1) + D] : 0.0f;
       } else {
-        sE[t] = b < b_end ? 1.0f : 0.0f;
-        sC[t] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
+        sE[q] = b < b_end ? 1.0f : 0.0f;
+        sC[q] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
       }
     }
     __syncthreads();
@@ -384,27 +385,46 @@ __global__ __launch_bounds__(kBlock) void key_mean(const TK* K, double* kbar, in
 }
 
 // Column min / max of V: partials over kMinMaxRows rows, then a reduction.
+// Each thread reads 16-byte groups of one row; 256 threads cover
+// 256 / (D / G) rows per pass, G = elements per 16 bytes.
 template <typename TK, int D>
 __global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, float* part, int n, int nmm) {
-  __shared__ float smn[kBlock], smx[kBlock];
+  constexpr int G = 16 / sizeof(TK);
+  constexpr int NG = D / G;            // groups per row
+  constexpr int RP = kBlock / NG;      // rows per pass
+  __shared__ float smn[RP][D + 1], smx[RP][D + 1];
   const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
-  constexpr int PH = kBlock / D;
-  const int c = t % D, ph = t / D;
+  const int grp = t % NG, ph = t / NG;
   const int l0 = blk * kMinMaxRows, l1 = min(n, l0 + kMinMaxRows);
-  float mn = INFINITY, mx = -INFINITY;
-  for (int l = l0 + ph; l < l1; l += PH) {
-    const float x = Elem<TK>::f32(V, ((size_t)u * n + l) * D + c);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+  float mn[G], mx[G];
+#pragma unroll
+  for (int q = 0; q < G; ++q) { mn[q] = INFINITY; mx[q] = -INFINITY; }
+  for (int l = l0 + ph; l < l1; l += RP) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(V + ((size_t)u * n + l) * D + grp * G);
+    float x[G];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (G == 8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * q] = __uint_as_float(w[q] << 16);
+        x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) { mn[q] = fminf(mn[q], x[q]); mx[q] = fmaxf(mx[q], x[q]); }
   }
-  smn[t] = mn;
-  smx[t] = mx;
+#pragma unroll
+  for (int q = 0; q < G; ++q) { smn[ph][grp * G + q] = mn[q]; smx[ph][grp * G + q] = mx[q]; }
   __syncthreads();
-  if (t < D) {
-    for (int q = 1; q < PH; ++q) { mn = fminf(mn, smn[q * D + t]); mx = fmaxf(mx, smx[q * D + t]); }
+  for (int c = t; c < D; c += kBlock) {
+    float a = INFINITY, b = -INFINITY;
+    for (int p = 0; p < RP; ++p) { a = fminf(a, smn[p][c]); b = fmaxf(b, smx[p][c]); }
     float* o = part + (((size_t)u * nmm + blk) * 2) * D;
-    o[t] = mn;
-    o[D + t] = mx;
+    o[c] = a;
+    o[D + c] = b;
   }
 }
 
@@ -423,19 +443,26 @@ __global__ __launch_bounds__(kBlock) void value_range_final(const float* part, f
 }
 
 // ---------------------------------------------------------------- host side
+// Grid: x = splits of the right rows, y = tiles of 64 left rows, z = units.
 template <int D, int MODE>
-static void launch_expmm(bool bf16, const ContractArgs& a, dim3 grid, hipStream_t st) {
-  if (bf16) expmm_bf16<D, MODE><<<grid, kBlock, 0, st>>>(a);
-  else expmm_f32<D, MODE><<<grid, kBlock, 0, st>>>(a);
+static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream_t st) {
+  const int tiles64 = (a.rowsA + 63) / 64;
+  if (bf16) {
+    const dim3 grid(nsplit, tiles64, a.units);
+    expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);
+  } else {
+    const dim3 grid(nsplit, tiles64, a.units);
+    expmm_f32<D, MODE><<<grid, kBlock, 0, st>>>(a);
+  }
 }
 
 template <int MODE>
-static hipError_t launch_expmm_d(bool bf16, int d, const ContractArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t launch_expmm_d(bool bf16, int d, const ContractArgs& a, int nsplit, hipStream_t st) {
   switch (d) {
-    case 16: launch_expmm<16, MODE>(bf16, a, grid, st); break;
-    case 32: launch_expmm<32, MODE>(bf16, a, grid, st); break;
-    case 64: launch_expmm<64, MODE>(bf16, a, grid, st); break;
-    case 128: launch_expmm<128, MODE>(bf16, a, grid, st); break;
+    case 16: launch_expmm<16, MODE>(bf16, a, nsplit, st); break;
+    case 32: launch_expmm<32, MODE>(bf16, a, nsplit, st); break;
+    case 64: launch_expmm<64, MODE>(bf16, a, nsplit, st); break;
+    case 128: launch_expmm<128, MODE>(bf16, a, nsplit, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -474,7 +501,7 @@ static hipError_t launch_prep_d(int d, int U, int n, int r, double c, int recent
   return hipGetLastError();
 }
 
-hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L,
+hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
                        const int32_t* r_eff, float* X, hipStream_t st);
 
 // CompressKV after selection: K_S, value range, Y = h_tau(K_S, K) [V, 1], X.
@@ -493,10 +520,9 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
   a.out = reinterpret_cast<float*>(w + lay.ypart);
   a.rowsA = r; a.rowsB = n; a.chunk = lay.sp.chunk; a.group = 1; a.units = U;
   a.scale = (float)c;
-  const dim3 grid(lay.sp.nsplit, lay.sp.tiles_a, U);
-  e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, grid, st);
+  e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, lay.sp.nsplit, st);
   if (e != hipSuccess) return e;
-  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, r_eff, X, st);
+  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, reinterpret_cast<double*>(w + lay.LT), r_eff, X, st);
 }
 
 // WtdAttn: O = clip(h(Q, K_S) X / (h(Q, K_S) w)).
@@ -507,8 +533,7 @@ hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, doubl
   a.A = Q; a.B = K_S; a.Vs = X; a.out = O; a.vmin = vmin; a.vmax = vmax;
   a.rowsA = m; a.rowsB = r; a.chunk = r; a.group = group; a.units = Uq;
   a.scale = (float)beta;
-  const dim3 grid(1, (m + kTileRows - 1) / kTileRows, Uq);
-  return launch_expmm_d<kModeAttend>(bf16 != 0, d, a, grid, st);
+  return launch_expmm_d<kModeAttend>(bf16 != 0, d, a, 1, st);
 }
 
 }  // namespace wc

@@ -7,23 +7,24 @@
 namespace wc {
 
 constexpr int kSelRowsPerThread = 2;                        // fp64 rows per lane in the step kernel
-constexpr int kSelRowsPerBlock = 256 * kSelRowsPerThread;   // rows of one workgroup = one scan block
+constexpr int kSelRowsPerBlock = 64 * kSelRowsPerThread;    // rows of one workgroup (one wave's lanes) = one scan block
 constexpr int kMaxR = 4096;
 constexpr int kMaxN = 1 << 21;
 
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 // RPNys workspace for U units of n keys, rank r, head dim d.
-//   F      [U][r][npad] fp64   factor, row i = column i of the Cholesky factor
+//   F      [U][nb][r][128] fp64  factor, block-major: slab (u, blk) holds columns
+//                                 0..r-1 of the Cholesky factor for that block's 128 keys
 //   dres   [U][npad]    fp64   residual diagonal (0 on padding rows)
 //   bsum   [U][nb]      fp64   per-workgroup residual sums of the last step
 //   pivbuf [U][2][pbs]  fp64   next pivot: s, sqrt(g_s), F[s,:i], k_s (double buffered by step parity)
 //   T0     [U]          fp64   initial residual trace
 //   kbar   [U][d]       fp64   key mean (recentring only)
-//   stopped, reff, counter [U] int32 / int32 / uint32
+//   stopped, reff [U] int32
 struct SelectLayout {
   int nb, npad, pbs;
-  size_t F, dres, bsum, pivbuf, T0, kbar, stopped, reff, counter, total;
+  size_t F, dres, bsum, pivbuf, T0, kbar, stopped, reff, total;
   SelectLayout(int U, int n, int d, int r) {
     nb = (n + kSelRowsPerBlock - 1) / kSelRowsPerBlock;
     npad = nb * kSelRowsPerBlock;
@@ -37,7 +38,6 @@ struct SelectLayout {
     kbar = o;    o += al256((size_t)U * d * 8);
     stopped = o; o += al256((size_t)U * 4);
     reff = o;    o += al256((size_t)U * 4);
-    counter = o; o += al256((size_t)U * 4);
     total = o;
   }
 };
@@ -64,11 +64,12 @@ struct ContractSplit {
 //   kbar    [U][d]              fp64   key mean (recentring only)
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
+//   LT      [U][r][r]           fp64   transposed pivot block for the forward solve
 constexpr int kMinMaxRows = 1024;   // rows of V per min/max partial
 struct WeightsLayout {
   ContractSplit sp;
   int nmm;
-  size_t ypart, mmpart, kbar, rowc, colc, total;
+  size_t ypart, mmpart, kbar, rowc, colc, LT, total;
   WeightsLayout(int U, int n, int d, int r) : sp(U, r, n) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
     size_t o = 0;
@@ -77,6 +78,7 @@ struct WeightsLayout {
     kbar = o;   o += al256((size_t)U * d * 8);
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
+    LT = o;     o += al256((size_t)U * r * r * 8);
     total = o;
   }
 };

@@ -8,19 +8,28 @@
 // the diagonal and n kernel entries per round are touched (O(nr) entries).
 //
 // GPU structure (one launch per round, all units in one grid):
-//   * workgroup (blk, u) owns 512 consecutive keys of unit u, two per lane;
-//     the factor F is stored [u][i][npad] so a round's read of F[:i] streams
-//     i contiguous 4 KiB slabs per workgroup with 16-byte loads;
+//   * workgroup (blk, u) owns 128 consecutive keys of unit u, two per lane;
+//     its 4 waves split the previous factor columns j < i (and the key
+//     dimensions) into quarters, so every wave streams its own contiguous run
+//     of 1 KiB factor segments with 16-byte loads; the partial sums meet in
+//     LDS and are combined in a fixed order;
+//   * the factor F is stored block-major, [u][blk][j][128]: everything one
+//     workgroup ever reads or writes of F is one contiguous region, and a
+//     round streams it front to back (one 1 KiB row per column j);
 //   * the pivot row F[s, :i] and k_s sit in LDS and are read as broadcasts;
-//   * each workgroup writes its slice of the new residual diagonal and a
-//     deterministic in-workgroup prefix-sum total; the last workgroup of a unit
-//     to finish (device-scope counter) draws the next pivot with a two-level
-//     inverse CDF over those totals and gathers F[s, :i+1] and k_s for the
-//     next launch, so the next round starts with its pivot ready.
+//   * wave 0 finishes the rows: kernel value, new factor column, residual
+//     downdate, and a wave-level inclusive prefix sum of the new residuals
+//     whose total goes to a per-workgroup slot;
+//   * a separate one-workgroup-per-unit launch then draws the next pivot with
+//     a two-level inverse CDF over those totals and gathers F[s, :i+1] and
+//     k_s for the next round.  Splitting the draw off keeps the streaming
+//     kernel free of device-scope fences and atomics (on gfx950 every
+//     device-scope release fence writes back the XCD's L2); the kernel
+//     boundary publishes the round's results once.
 // The draw is in fp64 with a fixed summation order: the prefix C_l of an index
 // is (exclusive prefix of its workgroup total) + (in-workgroup inclusive
 // prefix), T is C of the last index, and the pivot is the first l with
-// C_l > u_i T -- the same rule as the oracle, up to rounding of the sums.
+// C_l > u_i T -- the oracle's rule, up to the rounding of the sums.
 #include <climits>
 
 #include "common.hpp"
@@ -33,7 +42,7 @@ struct SelectArgs {
   const double* u;      // [U][r]
   int32_t* S;           // [U][r]
   double* L;            // [U][r][r]
-  double* F;            // [U][r][npad]
+  double* F;            // [U][nb][r][RB] (block-major factor)
   double* dres;         // [U][npad]
   double* bsum;         // [U][nb]
   double* pivbuf;       // [U][2][pbs]
@@ -41,19 +50,25 @@ struct SelectArgs {
   double* kbar;         // [U][D]
   int32_t* stopped;     // [U]
   int32_t* reff;        // [U]
-  uint32_t* counter;    // [U]
   int n, npad, nb, r, pbs;
   double c;             // beta / tau^2
 };
 
-constexpr int RPT = kSelRowsPerThread;
-constexpr int RB = kSelRowsPerBlock;
+constexpr int RB = kSelRowsPerBlock;   // 128 rows per workgroup, 2 per lane of one wave
 constexpr double kStopRel = 1e-12;
 
-// Eight consecutive key elements as float (one 16-byte load for bf16, two
-// for fp32).  Rows are 16-byte aligned: the C ABI checks the base pointer and
-// d*sizeof(elem) is a multiple of 16.
-__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+typedef double d2v __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ d2v ld2(const double* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const d2v*>(p));
+  return *reinterpret_cast<const d2v*>(p);
+}
+
+// Key elements as float: chunks of 8 (one 16-byte load for bf16, two for
+// fp32) or 4.  Row starts are 16-byte aligned (aligned base, d*elem % 16 == 0).
+template <int N> __device__ __forceinline__ void loadk(const bf16_t* p, float (&x)[N]);
+template <> __device__ __forceinline__ void loadk<8>(const bf16_t* p, float (&x)[8]) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -62,53 +77,65 @@ __device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
     x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
   }
 }
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+template <> __device__ __forceinline__ void loadk<4>(const bf16_t* p, float (&x)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+template <int N> __device__ __forceinline__ void loadk(const float* p, float (&x)[N]) {
+#pragma unroll
+  for (int q = 0; q < N; q += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p + q);
+    x[q] = a.x; x[q + 1] = a.y; x[q + 2] = a.z; x[q + 3] = a.w;
+  }
 }
 
-// <k_l - kbar, ks> in fp64 for one key row; 4 partial sums in a fixed order.
-template <typename TK, int D, bool RC>
-__device__ __forceinline__ double key_dot(const TK* krow, const double* ks, const double* kbar) {
+// sum_{c in [c0, c0+CN)} (k[c] - kbar[c]) * y[c] in fp64, 4 partial sums.
+// SQ: y = k - kbar itself (squared norm).
+template <typename TK, int CN, bool RC, bool SQ>
+__device__ __forceinline__ double key_part(const TK* krow, int c0, const double* y, const double* kbar) {
+  constexpr int CH = CN >= 8 ? 8 : 4;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll 2
-  for (int c = 0; c < D; c += 8) {
-    float x[8];
-    load8(krow + c, x);
+  for (int c = c0; c < c0 + CN; c += CH) {
+    float x[CH];
+    loadk<CH>(krow + c, x);
 #pragma unroll
-    for (int j = 0; j < 8; j += 4) {
+    for (int j = 0; j < CH; j += 4) {
       double x0 = x[j], x1 = x[j + 1], x2 = x[j + 2], x3 = x[j + 3];
       if (RC) { x0 -= kbar[c + j]; x1 -= kbar[c + j + 1]; x2 -= kbar[c + j + 2]; x3 -= kbar[c + j + 3]; }
-      a0 = fma(x0, ks[c + j + 0], a0);
-      a1 = fma(x1, ks[c + j + 1], a1);
-      a2 = fma(x2, ks[c + j + 2], a2);
-      a3 = fma(x3, ks[c + j + 3], a3);
+      a0 = fma(x0, SQ ? x0 : y[c + j + 0], a0);
+      a1 = fma(x1, SQ ? x1 : y[c + j + 1], a1);
+      a2 = fma(x2, SQ ? x2 : y[c + j + 2], a2);
+      a3 = fma(x3, SQ ? x3 : y[c + j + 3], a3);
     }
   }
   return (a0 + a1) + (a2 + a3);
 }
 
-// ||k_l - kbar||^2 in fp64.
-template <typename TK, int D, bool RC>
-__device__ __forceinline__ double key_sqnorm(const TK* krow, const double* kbar) {
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-#pragma unroll 2
-  for (int c = 0; c < D; c += 8) {
-    float x[8];
-    load8(krow + c, x);
+// In-workgroup inclusive prefix of the 128 residuals, run by one wave (two
+// per lane, lane-major).  Owner and selector both use this to get identical
+// bits.  Returns the total in every lane.
+__device__ __forceinline__ double wave_scan_rows(double (&v)[2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  v[1] += v[0];
+  const double incl = wave_incl_scan(v[1]);
+  double ex = __shfl_up(incl, 1, kWave);
+  if (lane == 0) ex = 0.0;
+  v[0] = ex + v[0];
+  v[1] = ex + v[1];
+  return __shfl(v[1], kWave - 1, kWave);
+}
+
+__device__ __forceinline__ int wave_min_int(int x) {
 #pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      double x0 = x[j], x1 = x[j + 1], x2 = x[j + 2], x3 = x[j + 3];
-      if (RC) { x0 -= kbar[c + j]; x1 -= kbar[c + j + 1]; x2 -= kbar[c + j + 2]; x3 -= kbar[c + j + 3]; }
-      a0 = fma(x0, x0, a0);
-      a1 = fma(x1, x1, a1);
-      a2 = fma(x2, x2, a2);
-      a3 = fma(x3, x3, a3);
-    }
-  }
-  return (a0 + a1) + (a2 + a3);
+  for (int off = kWave / 2; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, kWave));
+  return x;
 }
 
 __device__ __forceinline__ void mark_stopped(const SelectArgs& a, int u, int i) {
@@ -120,11 +147,11 @@ __device__ __forceinline__ void mark_stopped(const SelectArgs& a, int u, int i) 
 
 // Prefix of the workgroup totals in rounds of 256 (fixed order).  Calls
 // visit(b, P_b, bsum_b) for every block b of the unit, with P_b the exclusive
-// prefix, and returns T = P_{nb-1} + bsum_{nb-1}.  Every thread gets T.
+// prefix, and returns T = P_{nb-1} + bsum_{nb-1} in every thread.
 template <typename Visit>
 __device__ __forceinline__ double scan_block_totals(const SelectArgs& a, int u, double* scr, Visit visit) {
   const double* bs = a.bsum + (size_t)u * a.nb;
-  double carry = 0.0, T = 0.0;
+  double carry = 0.0;
   for (int base = 0; base < a.nb; base += kBlock) {
     const int b = base + (int)threadIdx.x;
     const double x = b < a.nb ? bs[b] : 0.0;
@@ -138,20 +165,21 @@ __device__ __forceinline__ double scan_block_totals(const SelectArgs& a, int u, 
     carry = carry + tot;
   }
   __syncthreads();
-  T = scr[kWavesPerBlock + 1];
+  const double T = scr[kWavesPerBlock + 1];
   __syncthreads();
   return T;
 }
 
 // Draw pivot i of unit u and stage it for the launch of round i.  Run by all
-// threads of the unit's last workgroup of round i-1 (or of the init kernel).
+// threads of one workgroup after round i-1 (or the initial diagonal).
 template <typename TK, int D, bool RC>
 __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, double* smem) {
   double* scr = smem;                              // 16 doubles
   int* iscr = reinterpret_cast<int*>(smem + 16);   // 8 ints
   double* sP = smem + 24;                          // 1 double
+  int* sS = reinterpret_cast<int*>(smem + 25);     // 1 int
   double* ks = smem + 32;                          // D doubles
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
 
   // Pass 1: total residual T.
   const double T = scan_block_totals(a, u, scr, [](int, double, double) {});
@@ -160,7 +188,8 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
   if (!(T > kStopRel * T0)) { mark_stopped(a, u, i); return; }
   const double target = a.u[(size_t)u * a.r + i] * T;
 
-  // Pass 2: first block whose last prefix exceeds the target.
+  // Pass 2: first block whose last prefix exceeds the target (or, if rounding
+  // leaves none, the last block with mass).
   int myb = INT_MAX, mypos = -1;
   double myP = 0.0;
   scan_block_totals(a, u, scr, [&](int b, double P, double x) {
@@ -175,30 +204,31 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
   __syncthreads();
   const double Pb = fallback ? 0.0 : *sP;
 
-  // Rescan the chosen block exactly as its owner did.
-  const double* du = a.dres + (size_t)u * a.npad;
-  const int row0 = bsel * RB + t * RPT;
-  double v[RPT], ex[RPT], tot;
+  // Rescan the chosen block exactly as its owner did (wave 0): first index
+  // with mass whose prefix exceeds the target; the last index with mass in
+  // the block if rounding leaves none (and always in the fallback case).
+  if (t < kWave) {
+    const double* du = a.dres + (size_t)u * a.npad;
+    const int row0 = bsel * RB + lane * 2;
+    const d2v d0 = *reinterpret_cast<const d2v*>(du + row0);
+    double v[2] = {d0.x, d0.y};
+    wave_scan_rows(v);
+    int cand = INT_MAX, lastpos = -1;
+    const double dv[2] = {d0.x, d0.y};
 #pragma unroll
-  for (int k = 0; k < RPT; ++k) v[k] = du[row0 + k];
-  double dv[RPT];
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) dv[k] = v[k];
-  block_scan<RPT>(v, ex, tot, scr);
-  // First index with mass whose prefix exceeds the target; the last index
-  // with mass in the block if rounding across lanes leaves none (and always
-  // in the fallback case).  Either way s is a valid index with d_s > 0.
-  int cand = INT_MAX, lastpos = -1;
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int l = row0 + k;
-    if (l < a.n && dv[k] > 0.0) {
-      lastpos = l;
-      if (!fallback && Pb + v[k] > target && l < cand) cand = l;
+    for (int k = 0; k < 2; ++k) {
+      const int l = row0 + k;
+      if (l < a.n && dv[k] > 0.0) {
+        lastpos = l;
+        if (!fallback && Pb + v[k] > target && l < cand) cand = l;
+      }
     }
+    cand = wave_min_int(cand);
+    lastpos = wave_max_int(lastpos);
+    if (lane == 0) *sS = cand != INT_MAX ? cand : lastpos;
   }
-  int s = block_min_int(cand, iscr);
-  if (s == INT_MAX) s = block_max_int(lastpos, iscr);
+  __syncthreads();
+  const int s = *sS;
   if (s < 0) { mark_stopped(a, u, i); return; }
 
   // Stage k_s (recentred) and the pivot row F[s, :i]; write row i of L.
@@ -210,12 +240,12 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
     ks[c] = x;
     pb[2 + a.r + c] = x;
   }
-  const double* Fu = a.F + (size_t)u * a.r * a.npad;
+  const double* Fs = a.F + (((size_t)u * a.nb + s / RB) * a.r) * RB + (s % RB);
   double* Lrow = a.L + ((size_t)u * a.r + i) * a.r;
   double sq = 0.0;
   for (int j = t; j < a.r; j += kBlock) {
     if (j < i) {
-      const double f = Fu[(size_t)j * a.npad + s];
+      const double f = Fs[(size_t)j * RB];
       pb[2 + j] = f;
       Lrow[j] = f;
       sq = fma(f, f, sq);
@@ -237,30 +267,11 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
   }
 }
 
-// Unit's last workgroup detection: every thread fences its own stores, then
-// one atomic per workgroup.  Returns true in all threads of the last one.
-__device__ __forceinline__ bool last_block_of_unit(const SelectArgs& a, int u, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counter[u], 1u);
-    *flag = (prev == (unsigned)a.nb - 1u) ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) {
-    __threadfence();
-    if (threadIdx.x == 0) a.counter[u] = 0u;
-  }
-  return last;
-}
-
 __global__ __launch_bounds__(kBlock) void rpc_clear(SelectArgs a, int U) {
   const int u = blockIdx.x * kBlock + threadIdx.x;
   if (u < U) {
     a.stopped[u] = 0;
     a.reff[u] = a.r;
-    a.counter[u] = 0u;
   }
 }
 
@@ -283,42 +294,52 @@ __global__ __launch_bounds__(kBlock) void rpc_kbar(SelectArgs a) {
   }
 }
 
-// Residual diagonal h_tau(k_l, k_l), its block totals, and pivot 0.
+// Residual diagonal h_tau(k_l, k_l) and its block totals.
 template <typename TK, int D, bool RC>
 __global__ __launch_bounds__(kBlock) void rpc_init(SelectArgs a) {
   extern __shared__ double smem[];
   double* s_kbar = smem + 32 + D;
-  __shared__ int flag;
   const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
   if (RC) {
     for (int c = t; c < D; c += kBlock) s_kbar[c] = a.kbar[(size_t)u * D + c];
     __syncthreads();
   }
-  const TK* K = reinterpret_cast<const TK*>(a.K) + (size_t)u * a.n * D;
-  double* du = a.dres + (size_t)u * a.npad;
-  const int row0 = blk * RB + t * RPT;
-  double v[RPT], ex[RPT], tot;
+  if (t < kWave) {
+    const TK* K = reinterpret_cast<const TK*>(a.K) + (size_t)u * a.n * D;
+    double* du = a.dres + (size_t)u * a.npad;
+    const int row0 = blk * RB + t * 2;
+    double v[2];
 #pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int l = row0 + k;
-    v[k] = l < a.n ? exp(a.c * key_sqnorm<TK, D, RC>(K + (size_t)l * D, s_kbar)) : 0.0;
-    du[l] = v[k];
+    for (int k = 0; k < 2; ++k) {
+      const int l = row0 + k;
+      v[k] = l < a.n ? exp(a.c * key_part<TK, D, RC, true>(K + (size_t)l * D, 0, nullptr, s_kbar)) : 0.0;
+    }
+    *reinterpret_cast<d2v*>(du + row0) = d2v{v[0], v[1]};
+    const double tot = wave_scan_rows(v);
+    if (t == 0) a.bsum[(size_t)u * a.nb + blk] = tot;
   }
-  block_scan<RPT>(v, ex, tot, smem);
-  if (t == 0) a.bsum[(size_t)u * a.nb + blk] = tot;
-  if (!last_block_of_unit(a, u, &flag)) return;
-  draw_and_stage<TK, D, RC>(a, u, 0, true, smem);
+}
+
+// Pivot i of every running unit (one workgroup per unit).
+template <typename TK, int D, bool RC>
+__global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
+  extern __shared__ double smem[];
+  const int u = blockIdx.x;
+  if (a.stopped[u]) return;
+  draw_and_stage<TK, D, RC>(a, u, i, i == 0, smem);
 }
 
 // One RPNys round i for every unit still running.
-template <typename TK, int D, bool RC>
+template <typename TK, int D, bool RC, bool NT>
 __global__ __launch_bounds__(kBlock) void rpc_step(SelectArgs a, int i) {
   extern __shared__ double smem[];
-  double* s_ks = smem + 32;            // D
-  double* s_kbar = s_ks + D;           // D
-  double* s_prow = s_kbar + D;         // r
-  __shared__ int flag;
+  double* s_ks = smem + 32;              // D
+  double* s_kbar = s_ks + D;             // D
+  double* s_pf = s_kbar + D;             // [4][RB] factor partials
+  double* s_pk = s_pf + 4 * RB;          // [4][RB] key partials
+  double* s_prow = s_pk + 4 * RB;        // r
   const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+  const int wave = t / kWave, lane = t & (kWave - 1);
   if (a.stopped[u]) return;
   const double* pb = a.pivbuf + ((size_t)u * 2 + (i & 1)) * a.pbs;
   const int s = (int)pb[0];
@@ -330,58 +351,89 @@ __global__ __launch_bounds__(kBlock) void rpc_step(SelectArgs a, int i) {
   }
   __syncthreads();
 
-  const int row0 = blk * RB + t * RPT;
-  double* Fu = a.F + (size_t)u * a.r * a.npad;
-  double* du = a.dres + (size_t)u * a.npad;
-  double v[RPT] = {0.0, 0.0}, ex[RPT], tot;
-  if (row0 < a.n) {
-    // sum_j F[j][l] * F[s][j] for the thread's two rows, 4 partial sums each.
-    double p0x = 0.0, p0y = 0.0, p1x = 0.0, p1y = 0.0, p2x = 0.0, p2y = 0.0, p3x = 0.0, p3y = 0.0;
-    const double* Fr = Fu + row0;
-    const size_t ld = (size_t)a.npad;
-    int j = 0;
-    for (; j + 4 <= i; j += 4) {
-      const double2 f0 = *reinterpret_cast<const double2*>(Fr + (size_t)(j + 0) * ld);
-      const double2 f1 = *reinterpret_cast<const double2*>(Fr + (size_t)(j + 1) * ld);
-      const double2 f2 = *reinterpret_cast<const double2*>(Fr + (size_t)(j + 2) * ld);
-      const double2 f3 = *reinterpret_cast<const double2*>(Fr + (size_t)(j + 3) * ld);
-      const double q0 = s_prow[j], q1 = s_prow[j + 1], q2 = s_prow[j + 2], q3 = s_prow[j + 3];
-      p0x = fma(f0.x, q0, p0x); p0y = fma(f0.y, q0, p0y);
-      p1x = fma(f1.x, q1, p1x); p1y = fma(f1.y, q1, p1y);
-      p2x = fma(f2.x, q2, p2x); p2y = fma(f2.y, q2, p2y);
-      p3x = fma(f3.x, q3, p3x); p3y = fma(f3.y, q3, p3y);
-    }
-    for (; j < i; ++j) {
-      const double2 f0 = *reinterpret_cast<const double2*>(Fr + (size_t)j * ld);
-      const double q0 = s_prow[j];
-      p0x = fma(f0.x, q0, p0x); p0y = fma(f0.y, q0, p0y);
-    }
-    const double accx = (p0x + p1x) + (p2x + p3x);
-    const double accy = (p0y + p1y) + (p2y + p3y);
+  const int row0 = blk * RB + lane * 2;
+  const bool live = row0 < a.n;
+  const bool has_y = row0 + 1 < a.n;
+  double* Fb = a.F + ((size_t)u * a.nb + blk) * a.r * RB;   // this workgroup's [r][RB] slab
+  constexpr size_t ld = RB;
 
-    const TK* K = reinterpret_cast<const TK*>(a.K) + (size_t)u * a.n * D;
-    const double gx = exp(a.c * key_dot<TK, D, RC>(K + (size_t)row0 * D, s_ks, s_kbar)) - accx;
-    const bool has_y = row0 + 1 < a.n;
-    const double gy = has_y ? exp(a.c * key_dot<TK, D, RC>(K + (size_t)(row0 + 1) * D, s_ks, s_kbar)) - accy : 0.0;
-    const double fx = gx / sgs;
-    const double fy = has_y ? gy / sgs : 0.0;
-    *reinterpret_cast<double2*>(Fu + (size_t)i * ld + row0) = make_double2(fx, fy);
-    const double2 dold = *reinterpret_cast<const double2*>(du + row0);
-    const double fx2 = fx * fx, fy2 = fy * fy;
-    double dx = dold.x - fx2, dy = dold.y - fy2;
-    dx = dx > 0.0 ? dx : 0.0;
-    dy = dy > 0.0 ? dy : 0.0;
-    if (row0 == s) { dx = 0.0; a.L[((size_t)u * a.r + i) * a.r + i] = fx; }
-    if (row0 + 1 == s) { dy = 0.0; a.L[((size_t)u * a.r + i) * a.r + i] = fy; }
-    if (!has_y) dy = 0.0;
-    *reinterpret_cast<double2*>(du + row0) = make_double2(dx, dy);
-    v[0] = dx;
-    v[1] = dy;
+  // This wave's quarter of sum_j F[j][l] F[s][j] for the lane's two rows.
+  double fx = 0.0, fy = 0.0;
+  if (live) {
+    const int jb = (i * wave) >> 2, je = (i * (wave + 1)) >> 2;
+    const double* Fp = Fb + (size_t)jb * ld + 2 * lane;
+    double ax0 = 0.0, ay0 = 0.0, ax1 = 0.0, ay1 = 0.0, ax2 = 0.0, ay2 = 0.0, ax3 = 0.0, ay3 = 0.0;
+    int j = jb;
+    for (; j + 8 <= je; j += 8) {
+      d2v f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
+      Fp += 8 * ld;
+#pragma unroll
+      for (int q = 0; q < 8; q += 4) {
+        const double p0 = s_prow[j + q], p1 = s_prow[j + q + 1], p2 = s_prow[j + q + 2], p3 = s_prow[j + q + 3];
+        ax0 = fma(f[q].x, p0, ax0); ay0 = fma(f[q].y, p0, ay0);
+        ax1 = fma(f[q + 1].x, p1, ax1); ay1 = fma(f[q + 1].y, p1, ay1);
+        ax2 = fma(f[q + 2].x, p2, ax2); ay2 = fma(f[q + 2].y, p2, ay2);
+        ax3 = fma(f[q + 3].x, p3, ax3); ay3 = fma(f[q + 3].y, p3, ay3);
+      }
+    }
+    for (; j < je; ++j) {
+      const d2v f0 = ld2<NT>(Fp);
+      Fp += ld;
+      const double p0 = s_prow[j];
+      ax0 = fma(f0.x, p0, ax0); ay0 = fma(f0.y, p0, ay0);
+    }
+    fx = (ax0 + ax1) + (ax2 + ax3);
+    fy = (ay0 + ay1) + (ay2 + ay3);
   }
-  block_scan<RPT>(v, ex, tot, smem);
-  if (t == 0) a.bsum[(size_t)u * a.nb + blk] = tot;
-  if (!last_block_of_unit(a, u, &flag)) return;
-  if (i + 1 < a.r) draw_and_stage<TK, D, RC>(a, u, i + 1, false, smem);
+  // This wave's quarter of <k_l - kbar, k_s - kbar>.
+  constexpr int DQ = D / 4;
+  double kx = 0.0, ky = 0.0;
+  if (live) {
+    const TK* K = reinterpret_cast<const TK*>(a.K) + ((size_t)u * a.n + row0) * D;
+    kx = key_part<TK, DQ, RC, false>(K, wave * DQ, s_ks, s_kbar);
+    if (has_y) ky = key_part<TK, DQ, RC, false>(K + D, wave * DQ, s_ks, s_kbar);
+  }
+  s_pf[wave * RB + 2 * lane] = fx;
+  s_pf[wave * RB + 2 * lane + 1] = fy;
+  s_pk[wave * RB + 2 * lane] = kx;
+  s_pk[wave * RB + 2 * lane + 1] = ky;
+  __syncthreads();
+
+  if (wave == 0) {
+    double v[2] = {0.0, 0.0};
+    if (live) {
+      double* du = a.dres + (size_t)u * a.npad;
+      double g[2], fnew[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 2 * lane + k;
+        const double fd = (s_pf[e] + s_pf[RB + e]) + (s_pf[2 * RB + e] + s_pf[3 * RB + e]);
+        const double kd = (s_pk[e] + s_pk[RB + e]) + (s_pk[2 * RB + e] + s_pk[3 * RB + e]);
+        g[k] = exp(a.c * kd) - fd;
+      }
+      fnew[0] = g[0] / sgs;
+      fnew[1] = has_y ? g[1] / sgs : 0.0;
+      *reinterpret_cast<d2v*>(Fb + (size_t)i * ld + 2 * lane) = d2v{fnew[0], fnew[1]};
+      const d2v dold = *reinterpret_cast<const d2v*>(du + row0);
+      const double dd[2] = {dold.x, dold.y};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const double f2 = fnew[k] * fnew[k];
+        double dn = dd[k] - f2;
+        dn = dn > 0.0 ? dn : 0.0;
+        if (row0 + k == s) {
+          dn = 0.0;
+          a.L[((size_t)u * a.r + i) * a.r + i] = fnew[k];
+        }
+        v[k] = (k == 0 || has_y) ? dn : 0.0;
+      }
+      *reinterpret_cast<d2v*>(du + row0) = d2v{v[0], v[1]};
+    }
+    const double tot = wave_scan_rows(v);
+    if (lane == 0) a.bsum[(size_t)u * a.nb + blk] = tot;
+  }
 }
 
 // r_eff, -1 padding of S and zero rows of L past r_eff.
@@ -395,15 +447,24 @@ __global__ __launch_bounds__(kBlock) void rpc_finalize(SelectArgs a, int32_t* r_
   for (size_t e = from + t; e < to; e += kBlock) Lu[e] = 0.0;
 }
 
+#ifndef WILDCAT_SELECT_NT
+#define WILDCAT_SELECT_NT 0
+#endif
+
 template <typename TK, int D, bool RC>
 static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hipStream_t st) {
   const dim3 grid(a.nb, U);
   rpc_clear<<<(U + kBlock - 1) / kBlock, kBlock, 0, st>>>(a, U);
   if (RC) rpc_kbar<TK, D><<<U, kBlock, 0, st>>>(a);
   const size_t lds_init = (32 + 2 * D) * sizeof(double);
+  const size_t lds_draw = (32 + D) * sizeof(double);
+  const size_t lds_step = (32 + 2 * D + 8 * RB + a.r) * sizeof(double);
   rpc_init<TK, D, RC><<<grid, kBlock, lds_init, st>>>(a);
-  const size_t lds_step = (32 + 2 * D + a.r) * sizeof(double);
-  for (int i = 0; i < a.r; ++i) rpc_step<TK, D, RC><<<grid, kBlock, lds_step, st>>>(a, i);
+  rpc_draw<TK, D, RC><<<U, kBlock, lds_draw, st>>>(a, 0);
+  for (int i = 0; i < a.r; ++i) {
+    rpc_step<TK, D, RC, WILDCAT_SELECT_NT != 0><<<grid, kBlock, lds_step, st>>>(a, i);
+    if (i + 1 < a.r) rpc_draw<TK, D, RC><<<U, kBlock, lds_draw, st>>>(a, i + 1);
+  }
   rpc_finalize<<<U, kBlock, 0, st>>>(a, r_eff);
   return hipGetLastError();
 }
@@ -440,7 +501,6 @@ hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int rec
   a.kbar = reinterpret_cast<double*>(w + lay.kbar);
   a.stopped = reinterpret_cast<int32_t*>(w + lay.stopped);
   a.reff = reinterpret_cast<int32_t*>(w + lay.reff);
-  a.counter = reinterpret_cast<uint32_t*>(w + lay.counter);
   a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.c = c;
   return bf16 ? launch_select_d<bf16_t>(a, U, d, recentre != 0, r_eff, st)
               : launch_select_d<float>(a, U, d, recentre != 0, r_eff, st);
