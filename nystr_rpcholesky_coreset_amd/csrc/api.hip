@@ -43,7 +43,7 @@ size_t wildcat_select_workspace_bytes(const wildcat_kv_desc* desc) {
 
 size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc) {
   if (check_kv(desc) != WILDCAT_OK) return 0;
-  return wc::WeightsLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r).total;
+  return wc::WeightsLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r, desc->dtype == WILDCAT_BF16).total;
 }
 
 wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K, const double* u, int32_t* S,

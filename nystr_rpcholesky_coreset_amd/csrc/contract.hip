@@ -233,6 +233,221 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
   }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Physical LDS row of key k inside its 32-key block for the 32x32 kernel:
+// bits 2 and 3 of the index swapped (an involution).  With this placement the
+// 32x32x16 score MFMA leaves, in every lane, the probabilities of its own left
+// row for 8 consecutive keys per 16-key block -- the A-operand layout of the
+// value MFMA.
+__device__ __forceinline__ int perm32(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// Same contraction with v_mfma_f32_32x32x16_bf16: each wave owns 32 left rows,
+// NWAVE waves share double-buffered LDS tiles of 32 right rows (prefetched into
+// registers one tile ahead, one barrier per tile).  Per 32 right rows a wave
+// issues D/16 score MFMAs and 2*D/32 value MFMAs.  d >= 32.
+template <int D, int MODE, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
+  constexpr int NTH = 64 * NWAVE;
+  constexpr int KT = 32;                   // right rows per tile
+  constexpr int KP = D + 8;                // bf16 pitch of a right row in LDS
+  constexpr int VP = KT + 8;               // bf16 pitch of a transposed value row
+  constexpr int DK = D / 16;
+  constexpr int CT = D / 32;
+  constexpr int KI = KT * (D / 8);         // 16-byte right-row items per tile
+  constexpr int VI = (KT / 2) * (D / 8);   // value items: (row pair, 8 columns)
+  constexpr int KIPT = (KI + NTH - 1) / NTH;
+  constexpr int VIPT = (VI + NTH - 1) / NTH;
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][KT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sVT[2][D * VP];
+  __shared__ float sE[2][KT];
+  __shared__ float sC[2][KT];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g2 = lane >> 5, r32 = lane & 31;
+  const int unit = blockIdx.z, unitB = unit / p.group;
+  const int a0 = blockIdx.y * 32 * NWAVE;
+  const int split = blockIdx.x;
+  const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
+  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (size_t)unit * p.rowsA * D;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (size_t)unitB * p.rowsB * D;
+
+  // Left-row fragments (B operand of the score MFMA): row a0 + 32 wave + r32,
+  // d = 16 dk + 8 g2 .. +7.
+  const int arow = a0 + wave * 32 + r32;
+  bf16x8 afrag[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (arow < p.rowsA) v = *reinterpret_cast<const uint4*>(A + (size_t)arow * D + 16 * dk + 8 * g2);
+    afrag[dk] = __builtin_bit_cast(bf16x8, v);
+  }
+  float rc2 = 0.0f;
+  if (MODE == kModeWeights && p.rowc != nullptr && arow < p.rowsA) rc2 = p.rowc[(size_t)unit * p.rowsA + arow] * kLog2e;
+  const float sc2 = p.scale * kLog2e;
+
+  // ---- tile staging through registers
+  uint4 kreg[KIPT];
+  uint32_t vlo[VIPT][8], vhi[VIPT][8];
+  float ereg = 0.0f, creg = 0.0f;
+  auto load_tile = [&](int b0) {
+#pragma unroll
+    for (int q = 0; q < KIPT; ++q) {
+      const int it = t + q * NTH;
+      kreg[q] = make_uint4(0u, 0u, 0u, 0u);
+      if (it < KI) {
+        const int row = it / (D / 8), c8 = it % (D / 8), b = b0 + row;
+        if (b < b_end) kreg[q] = *reinterpret_cast<const uint4*>(B + (size_t)b * D + 8 * c8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < VIPT; ++q) {
+      const int it = t + q * NTH;
+      const int rp = it % (KT / 2), c8 = it / (KT / 2), b = b0 + 2 * rp;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { vlo[q][j] = 0u; vhi[q][j] = 0u; }
+      if (it < VI) {
+        if (MODE == kModeWeights) {
+          const uint16_t* V = reinterpret_cast<const uint16_t*>(p.Vs) + (size_t)unitB * p.rowsB * D;
+          uint4 x = make_uint4(0u, 0u, 0u, 0u), y = make_uint4(0u, 0u, 0u, 0u);
+          if (b < b_end) x = *reinterpret_cast<const uint4*>(V + (size_t)b * D + 8 * c8);
+          if (b + 1 < b_end) y = *reinterpret_cast<const uint4*>(V + (size_t)(b + 1) * D + 8 * c8);
+          const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vlo[q][2 * j] = xs[j] & 0xFFFFu; vlo[q][2 * j + 1] = xs[j] >> 16;
+            vhi[q][2 * j] = ys[j] & 0xFFFFu; vhi[q][2 * j + 1] = ys[j] >> 16;
+          }
+        } else {
+          const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = b < b_end ? X[(size_t)b * (D + 1) + 8 * c8 + j] : 0.0f;
+            const float y = b + 1 < b_end ? X[(size_t)(b + 1) * (D + 1) + 8 * c8 + j] : 0.0f;
+            vlo[q][j] = __builtin_bit_cast(uint16_t, (__bf16)x);
+            vhi[q][j] = __builtin_bit_cast(uint16_t, (__bf16)y);
+          }
+        }
+      }
+    }
+    if (t < KT) {
+      const int b = b0 + t;
+      if (MODE == kModeAttend) {
+        const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
+        ereg = b < b_end ? X[(size_t)b * (D + 1) + D] : 0.0f;
+        creg = 0.0f;
+      } else {
+        ereg = b < b_end ? 1.0f : 0.0f;
+        creg = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < KIPT; ++q) {
+      const int it = t + q * NTH;
+      if (it < KI) {
+        const int row = it / (D / 8), c8 = it % (D / 8);
+        *reinterpret_cast<uint4*>(&sB[buf][perm32(row) * KP + 8 * c8]) = kreg[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < VIPT; ++q) {
+      const int it = t + q * NTH;
+      if (it < VI) {
+        const int rp = it % (KT / 2), c8 = it / (KT / 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint32_t*>(&sVT[buf][(8 * c8 + j) * VP + 2 * rp]) = vlo[q][j] | (vhi[q][j] << 16);
+      }
+    }
+    if (t < KT) { sE[buf][t] = ereg; sC[buf][t] = creg; }
+  };
+
+  f32x16 oacc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[ct][v] = 0.0f;
+  float eacc = 0.0f;
+
+  if (b_begin < b_end) {
+    load_tile(b_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int b0 = b_begin; b0 < b_end; b0 += KT) {
+    const bool more = b0 + KT < b_end;
+    if (more) load_tile(b0 + KT);
+
+    f32x16 s = {};
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sB[buf][r32 * KP + 16 * dk + 8 * g2]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), afrag[dk], s, 0, 0, 0);
+    }
+    // s[v] = score of left row r32 with right row k(v) = 16 (v/8) + 8 g2 + v % 8
+    bf16x8 pfrag[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = 16 * (v >> 3) + 8 * g2 + (v & 7);
+      float arg = fmaf(s[v], sc2, rc2);
+      if (MODE == kModeWeights) arg += sC[buf][k];
+      const float pv = (b0 + k < b_end) ? exp2f(arg) : 0.0f;
+      const __bf16 h = (__bf16)pv;
+      pfrag[v >> 3][v & 7] = h;
+      eacc = fmaf((float)h, sE[buf][k], eacc);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sVT[buf][(32 * ct + r32) * VP + 16 * kb + 8 * g2]);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfrag[kb], __builtin_bit_cast(bf16x8, v), oacc[ct], 0, 0, 0);
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // eacc: partial over this lane's half of the keys -> full sum for row r32.
+  eacc += __shfl_xor(eacc, 32, 64);
+  // oacc[ct][v] = result for left row 8 (v/4) + 4 g2 + v % 4 (of the wave's 32),
+  // column 32 ct + r32.
+  if (MODE == kModeWeights) {
+    float* Y = p.out + ((size_t)split * p.units + unit) * p.rowsA * (D + 1);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = a0 + wave * 32 + 8 * (v >> 2) + 4 * g2 + (v & 3);
+      if (row < p.rowsA) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[(size_t)row * (D + 1) + 32 * ct + r32] = oacc[ct][v];
+      }
+    }
+    if (g2 == 0 && arow < p.rowsA) Y[(size_t)arow * (D + 1) + D] = eacc;
+  } else {
+    float* O = p.out + (size_t)unit * p.rowsA * D;
+    const float* vmn = p.vmin + (size_t)unitB * D;
+    const float* vmx = p.vmax + (size_t)unitB * D;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = 8 * (v >> 2) + 4 * g2 + (v & 3);
+      const float e = __shfl(eacc, rl, 64);
+      const int row = a0 + wave * 32 + rl;
+      if (row < p.rowsA) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c = 32 * ct + r32;
+          O[(size_t)row * D + c] = fminf(fmaxf(oacc[ct][v] / e, vmn[c]), vmx[c]);
+        }
+      }
+    }
+  }
+}
+
 // fp32 inputs: the same contraction on the vector ALU in fp32 (P is not
 // rounded).  A workgroup owns 64 left rows; thread (row, quarter) accumulates
 // every fourth output column of its row.
@@ -443,15 +658,26 @@ __global__ __launch_bounds__(kBlock) void value_range_final(const float* part, f
 }
 
 // ---------------------------------------------------------------- host side
-// Grid: x = splits of the right rows, y = tiles of 64 left rows, z = units.
+// Grid: x = splits of the right rows, y = tiles of left rows, z = units.
+// bf16 with d >= 32 runs the 32x32x16 kernel with 2, 4 or 8 waves (32 left
+// rows each, see mfma32_waves); bf16 d = 16 the 16x16x32 kernel; fp32 the
+// vector-ALU kernel.  contract_rows_per_wg gives the same tiling to the
+// workspace layout.
 template <int D, int MODE>
 static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream_t st) {
-  const int tiles64 = (a.rowsA + 63) / 64;
+  const int rows = contract_rows_per_wg(D, a.rowsA, bf16);
+  const dim3 grid(nsplit, (a.rowsA + rows - 1) / rows, a.units);
   if (bf16) {
-    const dim3 grid(nsplit, tiles64, a.units);
-    expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);
+    if constexpr (D >= 32) {
+      switch (mfma32_waves(a.rowsA)) {
+        case 8: expmm32<D, MODE, 8><<<grid, 512, 0, st>>>(a); break;
+        case 4: expmm32<D, MODE, 4><<<grid, 256, 0, st>>>(a); break;
+        default: expmm32<D, MODE, 2><<<grid, 128, 0, st>>>(a); break;
+      }
+    } else {
+      expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);
+    }
   } else {
-    const dim3 grid(nsplit, tiles64, a.units);
     expmm_f32<D, MODE><<<grid, kBlock, 0, st>>>(a);
   }
 }
@@ -501,14 +727,14 @@ static hipError_t launch_prep_d(int d, int U, int n, int r, double c, int recent
   return hipGetLastError();
 }
 
-hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
+hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, double* Y, const double* L, double* LT,
                        const int32_t* r_eff, float* X, hipStream_t st);
 
 // CompressKV after selection: K_S, value range, Y = h_tau(K_S, K) [V, 1], X.
 hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
                           const void* V, const int32_t* S, const int32_t* r_eff, const double* L, void* K_S,
                           float* X, float* vmin, float* vmax, void* ws, hipStream_t st) {
-  const WeightsLayout lay(U, n, d, r);
+  const WeightsLayout lay(U, n, d, r, bf16 != 0);
   char* w = static_cast<char*>(ws);
   hipError_t e = bf16 ? launch_prep_d<bf16_t>(d, U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st)
                       : launch_prep_d<float>(d, U, n, r, c, recentre, K, V, S, r_eff, K_S, lay, w, vmin, vmax, st);
@@ -522,7 +748,8 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
   a.scale = (float)c;
   e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, lay.sp.nsplit, st);
   if (e != hipSuccess) return e;
-  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, reinterpret_cast<double*>(w + lay.LT), r_eff, X, st);
+  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, reinterpret_cast<double*>(w + lay.Y), L,
+                     reinterpret_cast<double*>(w + lay.LT), r_eff, X, st);
 }
 
 // WtdAttn: O = clip(h(Q, K_S) X / (h(Q, K_S) w)).

@@ -42,15 +42,23 @@ struct SelectLayout {
   }
 };
 
-// Geometry of the exp-kernel contraction Y = h_tau(K_S, K) [V, 1].
-constexpr int kTileRows = 64;   // A rows (pivot keys or queries) per workgroup
-constexpr int kTileKeys = 64;   // B rows (keys or pivots) staged per iteration
+// Geometry of the exp-kernel contractions.
+constexpr int kTileRows = 64;   // left rows per workgroup of the 16x16 and fp32 kernels
+constexpr int kTileKeys = 64;   // right rows staged per iteration (chunks are multiples of this)
+
+// Waves per workgroup of the 32x32 bf16 kernel (32 left rows per wave).
+inline int mfma32_waves(int rowsA) { return rowsA > 128 ? 8 : (rowsA > 64 ? 4 : 2); }
+
+// Left rows one workgroup owns, for the kernel that a (d, dtype, rows) call uses.
+inline int contract_rows_per_wg(int d, int rowsA, bool bf16) {
+  return (bf16 && d >= 32) ? 32 * mfma32_waves(rowsA) : kTileRows;
+}
 
 struct ContractSplit {
   int tiles_a, nsplit, chunk;   // chunk: keys per split, multiple of kTileKeys
-  ContractSplit(int U, int r, int n) {
-    tiles_a = (r + kTileRows - 1) / kTileRows;
-    int want = (2048 + tiles_a * U - 1) / (tiles_a * U);
+  ContractSplit(int U, int r, int n, int rows_per_wg) {
+    tiles_a = (r + rows_per_wg - 1) / rows_per_wg;
+    int want = (512 + tiles_a * U - 1) / (tiles_a * U);
     int maxs = (n + kTileKeys - 1) / kTileKeys;
     nsplit = want < 1 ? 1 : (want > maxs ? maxs : want);
     chunk = ((n + nsplit - 1) / nsplit + kTileKeys - 1) / kTileKeys * kTileKeys;
@@ -65,12 +73,13 @@ struct ContractSplit {
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
 //   LT      [U][r][r]           fp64   transposed pivot block for the forward solve
+//   Y       [U][r][d+1]         fp64   summed contraction h_tau(K_S, K) [V, 1]
 constexpr int kMinMaxRows = 1024;   // rows of V per min/max partial
 struct WeightsLayout {
   ContractSplit sp;
   int nmm;
-  size_t ypart, mmpart, kbar, rowc, colc, LT, total;
-  WeightsLayout(int U, int n, int d, int r) : sp(U, r, n) {
+  size_t ypart, mmpart, kbar, rowc, colc, LT, Y, total;
+  WeightsLayout(int U, int n, int d, int r, bool bf16) : sp(U, r, n, contract_rows_per_wg(d, r, bf16)) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
     size_t o = 0;
     ypart = o;  o += al256((size_t)sp.nsplit * U * r * (d + 1) * 4);
@@ -79,6 +88,7 @@ struct WeightsLayout {
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
     LT = o;     o += al256((size_t)U * r * r * 8);
+    Y = o;      o += al256((size_t)U * r * (d + 1) * 8);
     total = o;
   }
 };

@@ -181,21 +181,42 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
   double* ks = smem + 32;                          // D doubles
   const int t = threadIdx.x, lane = t & (kWave - 1);
 
-  // Pass 1: total residual T.
-  const double T = scan_block_totals(a, u, scr, [](int, double, double) {});
-  if (is_init && t == 0) a.T0[u] = T;
-  const double T0 = is_init ? T : a.T0[u];
-  if (!(T > kStopRel * T0)) { mark_stopped(a, u, i); return; }
-  const double target = a.u[(size_t)u * a.r + i] * T;
-
-  // Pass 2: first block whose last prefix exceeds the target (or, if rounding
-  // leaves none, the last block with mass).
+  const double T0pre = is_init ? 0.0 : a.T0[u];
+  const double uu = a.u[(size_t)u * a.r + i];
   int myb = INT_MAX, mypos = -1;
-  double myP = 0.0;
-  scan_block_totals(a, u, scr, [&](int b, double P, double x) {
-    if (P + x > target && b < myb) { myb = b; myP = P; }
-    if (x > 0.0) mypos = b;
-  });
+  double myP = 0.0, T, target;
+  if (a.nb <= kBlock) {
+    // One pass: every thread holds at most one workgroup total.
+    const int b = t;
+    const double x = b < a.nb ? a.bsum[(size_t)u * a.nb + b] : 0.0;
+    double v[1] = {x}, ex[1], tot;
+    block_scan<1>(v, ex, tot, scr);
+    const double P = ex[0];
+    if (b == a.nb - 1) scr[kWavesPerBlock + 1] = P + x;
+    __syncthreads();
+    T = scr[kWavesPerBlock + 1];
+    __syncthreads();
+    if (is_init && t == 0) a.T0[u] = T;
+    const double T0 = is_init ? T : T0pre;
+    if (!(T > kStopRel * T0)) { mark_stopped(a, u, i); return; }
+    target = uu * T;
+    if (b < a.nb) {
+      if (P + x > target) { myb = b; myP = P; }
+      if (x > 0.0) mypos = b;
+    }
+  } else {
+    // Pass 1: total residual T; pass 2: recompute the same prefixes and find
+    // the first block whose last prefix exceeds the target.
+    T = scan_block_totals(a, u, scr, [](int, double, double) {});
+    if (is_init && t == 0) a.T0[u] = T;
+    const double T0 = is_init ? T : T0pre;
+    if (!(T > kStopRel * T0)) { mark_stopped(a, u, i); return; }
+    target = uu * T;
+    scan_block_totals(a, u, scr, [&](int b, double P, double x) {
+      if (P + x > target && b < myb) { myb = b; myP = P; }
+      if (x > 0.0) mypos = b;
+    });
+  }
   const int bstar = block_min_int(myb, iscr);
   const bool fallback = (bstar == INT_MAX);
   const int bsel = fallback ? block_max_int(mypos, iscr) : bstar;
@@ -329,9 +350,20 @@ __global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
   draw_and_stage<TK, D, RC>(a, u, i, i == 0, smem);
 }
 
+// Tuning knobs of the streaming loop (compile-time).
+#ifndef WILDCAT_SELECT_NT
+#define WILDCAT_SELECT_NT 1        // non-temporal factor loads (the factor is streamed once per round)
+#endif
+#ifndef WILDCAT_SELECT_UNROLL
+#define WILDCAT_SELECT_UNROLL 8    // factor loads in flight per lane
+#endif
+#ifndef WILDCAT_SELECT_MINWAVES
+#define WILDCAT_SELECT_MINWAVES 1  // minimum waves per SIMD the register budget must allow
+#endif
+
 // One RPNys round i for every unit still running.
 template <typename TK, int D, bool RC, bool NT>
-__global__ __launch_bounds__(kBlock) void rpc_step(SelectArgs a, int i) {
+__global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(SelectArgs a, int i) {
   extern __shared__ double smem[];
   double* s_ks = smem + 32;              // D
   double* s_kbar = s_ks + D;             // D
@@ -363,14 +395,15 @@ __global__ __launch_bounds__(kBlock) void rpc_step(SelectArgs a, int i) {
     const int jb = (i * wave) >> 2, je = (i * (wave + 1)) >> 2;
     const double* Fp = Fb + (size_t)jb * ld + 2 * lane;
     double ax0 = 0.0, ay0 = 0.0, ax1 = 0.0, ay1 = 0.0, ax2 = 0.0, ay2 = 0.0, ax3 = 0.0, ay3 = 0.0;
+    constexpr int UN = WILDCAT_SELECT_UNROLL;
     int j = jb;
-    for (; j + 8 <= je; j += 8) {
-      d2v f[8];
+    for (; j + UN <= je; j += UN) {
+      d2v f[UN];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
-      Fp += 8 * ld;
+      for (int q = 0; q < UN; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
+      Fp += UN * ld;
 #pragma unroll
-      for (int q = 0; q < 8; q += 4) {
+      for (int q = 0; q < UN; q += 4) {
         const double p0 = s_prow[j + q], p1 = s_prow[j + q + 1], p2 = s_prow[j + q + 2], p3 = s_prow[j + q + 3];
         ax0 = fma(f[q].x, p0, ax0); ay0 = fma(f[q].y, p0, ay0);
         ax1 = fma(f[q + 1].x, p1, ax1); ay1 = fma(f[q + 1].y, p1, ay1);
@@ -446,10 +479,6 @@ __global__ __launch_bounds__(kBlock) void rpc_finalize(SelectArgs a, int32_t* r_
   const size_t from = (size_t)re * a.r, to = (size_t)a.r * a.r;
   for (size_t e = from + t; e < to; e += kBlock) Lu[e] = 0.0;
 }
-
-#ifndef WILDCAT_SELECT_NT
-#define WILDCAT_SELECT_NT 0
-#endif
 
 template <typename TK, int D, bool RC>
 static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hipStream_t st) {

@@ -20,7 +20,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwildcat.so")
+# WILDCAT_LIBRARY may point at another build of the same library (e.g. a
+# tuning variant); by default the in-tree build next to this file is used.
+LIB_PATH = os.environ.get("WILDCAT_LIBRARY") or os.path.join(_HERE, "libwildcat.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nystr_rpcholesky_coreset_amd.build`")
