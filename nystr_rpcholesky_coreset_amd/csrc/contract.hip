@@ -20,6 +20,8 @@
 // one 16-byte LDS read.  The last column ([.., 1] or w) is accumulated on the
 // vector ALU from the same bf16-rounded P.  No running maximum is needed: the
 // exponents are bounded by the input-range contract.
+#include <type_traits>
+
 #include "common.hpp"
 #include "layout.hpp"
 
@@ -243,13 +245,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int perm32(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // Same contraction with v_mfma_f32_32x32x16_bf16: each wave owns 32 left rows,
-// NWAVE waves share double-buffered LDS tiles of 32 right rows (prefetched into
-// registers one tile ahead, one barrier per tile).  Per 32 right rows a wave
-// issues D/16 score MFMAs and 2*D/32 value MFMAs.  d >= 32.
-template <int D, int MODE, int NWAVE>
+// NWAVE waves share double-buffered LDS tiles of KT right rows (loaded into
+// registers one tile ahead, one barrier per tile; KT = 16 * NWAVE, so the
+// 8-wave configuration uses 139 KiB of the 160 KiB LDS and one tile of MFMA
+// work covers the next tile's load latency).  Per 32 right rows a wave issues
+// D/16 score MFMAs and 2*D/32 value MFMAs.  d >= 32.
+template <int D, int MODE, int NWAVE, bool RC>
 __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   constexpr int NTH = 64 * NWAVE;
-  constexpr int KT = 32;                   // right rows per tile
+#ifndef WILDCAT_MFMA32_KTMAX
+#define WILDCAT_MFMA32_KTMAX 128
+#endif
+  constexpr int KT = (16 * NWAVE < WILDCAT_MFMA32_KTMAX) ? 16 * NWAVE : WILDCAT_MFMA32_KTMAX;   // right rows per tile
   constexpr int KP = D + 8;                // bf16 pitch of a right row in LDS
   constexpr int VP = KT + 8;               // bf16 pitch of a transposed value row
   constexpr int DK = D / 16;
@@ -260,8 +267,8 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   constexpr int VIPT = (VI + NTH - 1) / NTH;
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][KT * KP];
   __shared__ __attribute__((aligned(16))) uint16_t sVT[2][D * VP];
-  __shared__ float sE[2][KT];
-  __shared__ float sC[2][KT];
+  __shared__ __attribute__((aligned(16))) float sE[2][KT];   // attend: w of each right row
+  __shared__ __attribute__((aligned(16))) float sC[2][KT];   // weights with recentring: per-key offsets
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g2 = lane >> 5, r32 = lane & 31;
@@ -287,82 +294,101 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   if (MODE == kModeWeights && p.rowc != nullptr && arow < p.rowsA) rc2 = p.rowc[(size_t)unit * p.rowsA + arow] * kLog2e;
   const float sc2 = p.scale * kLog2e;
 
-  // ---- tile staging through registers
-  uint4 kreg[KIPT];
-  uint32_t vlo[VIPT][8], vhi[VIPT][8];
+  // ---- tile staging through registers.  load_tile only issues loads into
+  // registers; everything that consumes them (packing, LDS stores) happens in
+  // store_tile after the compute, so the loads overlap one tile of MFMA work.
+  // Prefetch registers as vector values (never stack arrays).
+  typedef uint32_t kvec_t __attribute__((ext_vector_type(4 * KIPT)));
+  typedef uint32_t vvec_t __attribute__((ext_vector_type(8 * VIPT)));
+  typedef float xvec_t __attribute__((ext_vector_type(16 * VIPT)));
+  kvec_t kreg = {};           // right-row tile: 16 bytes per item
+  vvec_t vreg = {};           // weights: rows 2rp and 2rp+1, 8 bf16 columns each
+  xvec_t xreg = {};           // attend: the same 2 x 8 values of X in fp32
   float ereg = 0.0f, creg = 0.0f;
-  auto load_tile = [&](int b0) {
+  // Rows past b_end are read from the last valid row instead (no branches
+  // around the loads): their probabilities are masked to 0, so only
+  // finiteness matters.
+  auto load_tile = [&](int b0) __attribute__((always_inline)) {
+    const int blast = b_end - 1;
 #pragma unroll
     for (int q = 0; q < KIPT; ++q) {
       const int it = t + q * NTH;
-      kreg[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (it < KI) {
-        const int row = it / (D / 8), c8 = it % (D / 8), b = b0 + row;
-        if (b < b_end) kreg[q] = *reinterpret_cast<const uint4*>(B + (size_t)b * D + 8 * c8);
+      if (KI % NTH == 0 || it < KI) {
+        const int row = it / (D / 8), c8 = it % (D / 8);
+        const int b = min(b0 + row, blast);
+        const uint4 x = *reinterpret_cast<const uint4*>(B + (size_t)b * D + 8 * c8);
+        kreg[4 * q] = x.x; kreg[4 * q + 1] = x.y; kreg[4 * q + 2] = x.z; kreg[4 * q + 3] = x.w;
       }
     }
 #pragma unroll
     for (int q = 0; q < VIPT; ++q) {
       const int it = t + q * NTH;
-      const int rp = it % (KT / 2), c8 = it / (KT / 2), b = b0 + 2 * rp;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { vlo[q][j] = 0u; vhi[q][j] = 0u; }
-      if (it < VI) {
+      if (VI % NTH == 0 || it < VI) {
+        const int rp = it % (KT / 2), c8 = it / (KT / 2);
+        const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
         if (MODE == kModeWeights) {
           const uint16_t* V = reinterpret_cast<const uint16_t*>(p.Vs) + (size_t)unitB * p.rowsB * D;
-          uint4 x = make_uint4(0u, 0u, 0u, 0u), y = make_uint4(0u, 0u, 0u, 0u);
-          if (b < b_end) x = *reinterpret_cast<const uint4*>(V + (size_t)b * D + 8 * c8);
-          if (b + 1 < b_end) y = *reinterpret_cast<const uint4*>(V + (size_t)(b + 1) * D + 8 * c8);
-          const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vlo[q][2 * j] = xs[j] & 0xFFFFu; vlo[q][2 * j + 1] = xs[j] >> 16;
-            vhi[q][2 * j] = ys[j] & 0xFFFFu; vhi[q][2 * j + 1] = ys[j] >> 16;
-          }
+          const uint4 x = *reinterpret_cast<const uint4*>(V + (size_t)b * D + 8 * c8);
+          const uint4 y = *reinterpret_cast<const uint4*>(V + (size_t)b1 * D + 8 * c8);
+          vreg[8 * q] = x.x; vreg[8 * q + 1] = x.y; vreg[8 * q + 2] = x.z; vreg[8 * q + 3] = x.w;
+          vreg[8 * q + 4] = y.x; vreg[8 * q + 5] = y.y; vreg[8 * q + 6] = y.z; vreg[8 * q + 7] = y.w;
         } else {
           const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float x = b < b_end ? X[(size_t)b * (D + 1) + 8 * c8 + j] : 0.0f;
-            const float y = b + 1 < b_end ? X[(size_t)(b + 1) * (D + 1) + 8 * c8 + j] : 0.0f;
-            vlo[q][j] = __builtin_bit_cast(uint16_t, (__bf16)x);
-            vhi[q][j] = __builtin_bit_cast(uint16_t, (__bf16)y);
+            xreg[16 * q + j] = X[(size_t)b * (D + 1) + 8 * c8 + j];
+            xreg[16 * q + 8 + j] = X[(size_t)b1 * (D + 1) + 8 * c8 + j];
           }
         }
       }
     }
     if (t < KT) {
-      const int b = b0 + t;
+      const int b = min(b0 + t, blast);
       if (MODE == kModeAttend) {
         const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
-        ereg = b < b_end ? X[(size_t)b * (D + 1) + D] : 0.0f;
-        creg = 0.0f;
-      } else {
-        ereg = b < b_end ? 1.0f : 0.0f;
-        creg = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
+        ereg = X[(size_t)b * (D + 1) + D];
       }
+      if (RC) creg = p.colc[(size_t)unitB * p.rowsB + b];
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < KIPT; ++q) {
       const int it = t + q * NTH;
-      if (it < KI) {
+      if (KI % NTH == 0 || it < KI) {
         const int row = it / (D / 8), c8 = it % (D / 8);
-        *reinterpret_cast<uint4*>(&sB[buf][perm32(row) * KP + 8 * c8]) = kreg[q];
+        *reinterpret_cast<uint4*>(&sB[buf][perm32(row) * KP + 8 * c8]) =
+            make_uint4(kreg[4 * q], kreg[4 * q + 1], kreg[4 * q + 2], kreg[4 * q + 3]);
       }
     }
 #pragma unroll
     for (int q = 0; q < VIPT; ++q) {
       const int it = t + q * NTH;
-      if (it < VI) {
+      if (VI % NTH == 0 || it < VI) {
         const int rp = it % (KT / 2), c8 = it / (KT / 2);
+        uint32_t w[8];
+        if (MODE == kModeWeights) {
+          const uint32_t xs[4] = {vreg[8 * q], vreg[8 * q + 1], vreg[8 * q + 2], vreg[8 * q + 3]};
+          const uint32_t ys[4] = {vreg[8 * q + 4], vreg[8 * q + 5], vreg[8 * q + 6], vreg[8 * q + 7]};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint32_t*>(&sVT[buf][(8 * c8 + j) * VP + 2 * rp]) = vlo[q][j] | (vhi[q][j] << 16);
+          for (int j = 0; j < 4; ++j) {
+            w[2 * j] = (xs[j] & 0xFFFFu) | (ys[j] << 16);
+            w[2 * j + 1] = (xs[j] >> 16) | (ys[j] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            w[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[16 * q + j]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[16 * q + 8 + j]) << 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(&sVT[buf][(8 * c8 + j) * VP + 2 * rp]) = w[j];
       }
     }
-    if (t < KT) { sE[buf][t] = ereg; sC[buf][t] = creg; }
+    if (t < KT) {
+      if (MODE == kModeAttend) sE[buf][t] = ereg;
+      if (RC) sC[buf][t] = creg * kLog2e;
+    }
   };
 
   f32x16 oacc[CT];
@@ -372,6 +398,64 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     for (int v = 0; v < 16; ++v) oacc[ct][v] = 0.0f;
   float eacc = 0.0f;
 
+  // Scores of the wave's 32 left rows against right rows kofs .. kofs+31 of
+  // the tile in buffer `bf`: s[v] = <left r32, right kofs + k(v)>,
+  // k(v) = 16 (v/8) + 8 g2 + v % 8 (the perm32 placement).
+  auto scores = [&](int bf, int kofs) __attribute__((always_inline)) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sB[bf][(kofs + r32) * KP + 16 * dk + 8 * g2]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), afrag[dk], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  // Probabilities exp2(scale2 * s + offsets) as bf16 in the value MFMA's
+  // A-operand layout, and the last-column sum from the same rounded values.
+  auto probs = [&](auto masked_tag, const f32x16& sv, int bf, int kofs, int b0, bf16x8 (&pfrag)[2]) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    float ev[16], cv[16];
+    if (MODE == kModeAttend) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 e0 = *reinterpret_cast<const float4*>(&sE[bf][kofs + 16 * kb + 8 * g2]);
+        const float4 e1 = *reinterpret_cast<const float4*>(&sE[bf][kofs + 16 * kb + 8 * g2 + 4]);
+        ev[8 * kb + 0] = e0.x; ev[8 * kb + 1] = e0.y; ev[8 * kb + 2] = e0.z; ev[8 * kb + 3] = e0.w;
+        ev[8 * kb + 4] = e1.x; ev[8 * kb + 5] = e1.y; ev[8 * kb + 6] = e1.z; ev[8 * kb + 7] = e1.w;
+      }
+    }
+    if (RC) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 c0 = *reinterpret_cast<const float4*>(&sC[bf][kofs + 16 * kb + 8 * g2]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&sC[bf][kofs + 16 * kb + 8 * g2 + 4]);
+        cv[8 * kb + 0] = c0.x; cv[8 * kb + 1] = c0.y; cv[8 * kb + 2] = c0.z; cv[8 * kb + 3] = c0.w;
+        cv[8 * kb + 4] = c1.x; cv[8 * kb + 5] = c1.y; cv[8 * kb + 6] = c1.z; cv[8 * kb + 7] = c1.w;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float arg = fmaf(sv[v], sc2, rc2);
+      if (RC) arg += cv[v];
+      float pv = __builtin_amdgcn_exp2f(arg);
+      if (MASKED) pv = (b0 + kofs + 16 * (v >> 3) + 8 * g2 + (v & 7) < b_end) ? pv : 0.0f;
+      const __bf16 h = (__bf16)pv;
+      pfrag[v >> 3][v & 7] = h;
+      eacc = MODE == kModeAttend ? fmaf((float)h, ev[v], eacc) : eacc + (float)h;
+    }
+  };
+  // oacc += P (32 rows x 32 right rows) x V (32 right rows x D).
+  auto values = [&](int bf, int kofs, const bf16x8 (&pfrag)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sVT[bf][(32 * ct + r32) * VP + kofs + 16 * kb + 8 * g2]);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfrag[kb], __builtin_bit_cast(bf16x8, v), oacc[ct], 0, 0, 0);
+      }
+    }
+  };
+
   if (b_begin < b_end) {
     load_tile(b_begin);
     store_tile(0);
@@ -379,36 +463,26 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   __syncthreads();
   int buf = 0;
   for (int b0 = b_begin; b0 < b_end; b0 += KT) {
-    const bool more = b0 + KT < b_end;
-    if (more) load_tile(b0 + KT);
+    // Unconditional prefetch (the last tile re-loads itself into the idle
+    // buffer): keeps the loads out of branches so they stay in flight.
+    const int bnext = b0 + KT < b_end ? b0 + KT : b0;
+    load_tile(bnext);
 
-    f32x16 s = {};
+    // Software pipeline over the tile's 32-row blocks: the score MFMAs of
+    // block k+1 are issued before the probabilities of block k are computed,
+    // so the VALU work co-executes with the matrix core.
+    f32x16 s_next = scores(buf, 0);
+    const bool full_tile = b0 + KT <= b_end;
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sB[buf][r32 * KP + 16 * dk + 8 * g2]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), afrag[dk], s, 0, 0, 0);
+    for (int kb32 = 0; kb32 < KT / 32; ++kb32) {
+      const f32x16 s_cur = s_next;
+      if (kb32 + 1 < KT / 32) s_next = scores(buf, 32 * (kb32 + 1));
+      bf16x8 pfrag[2];
+      if (full_tile) probs(std::false_type{}, s_cur, buf, 32 * kb32, b0, pfrag);
+      else probs(std::true_type{}, s_cur, buf, 32 * kb32, b0, pfrag);
+      values(buf, 32 * kb32, pfrag);
     }
-    // s[v] = score of left row r32 with right row k(v) = 16 (v/8) + 8 g2 + v % 8
-    bf16x8 pfrag[2];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int k = 16 * (v >> 3) + 8 * g2 + (v & 7);
-      float arg = fmaf(s[v], sc2, rc2);
-      if (MODE == kModeWeights) arg += sC[buf][k];
-      const float pv = (b0 + k < b_end) ? exp2f(arg) : 0.0f;
-      const __bf16 h = (__bf16)pv;
-      pfrag[v >> 3][v & 7] = h;
-      eacc = fmaf((float)h, sE[buf][k], eacc);
-    }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sVT[buf][(32 * ct + r32) * VP + 16 * kb + 8 * g2]);
-        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfrag[kb], __builtin_bit_cast(bf16x8, v), oacc[ct], 0, 0, 0);
-      }
-    }
-    if (more) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
@@ -669,10 +743,16 @@ static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream
   const dim3 grid(nsplit, (a.rowsA + rows - 1) / rows, a.units);
   if (bf16) {
     if constexpr (D >= 32) {
-      switch (mfma32_waves(a.rowsA)) {
-        case 8: expmm32<D, MODE, 8><<<grid, 512, 0, st>>>(a); break;
-        case 4: expmm32<D, MODE, 4><<<grid, 256, 0, st>>>(a); break;
-        default: expmm32<D, MODE, 2><<<grid, 128, 0, st>>>(a); break;
+      const int nw = mfma32_waves(a.rowsA);
+      if (MODE == kModeWeights && a.colc != nullptr) {   // recentring offsets (weights only)
+        constexpr bool RC = MODE == kModeWeights;
+        if (nw == 8) expmm32<D, MODE, 8, RC><<<grid, 512, 0, st>>>(a);
+        else if (nw == 4) expmm32<D, MODE, 4, RC><<<grid, 256, 0, st>>>(a);
+        else expmm32<D, MODE, 2, RC><<<grid, 128, 0, st>>>(a);
+      } else {
+        if (nw == 8) expmm32<D, MODE, 8, false><<<grid, 512, 0, st>>>(a);
+        else if (nw == 4) expmm32<D, MODE, 4, false><<<grid, 256, 0, st>>>(a);
+        else expmm32<D, MODE, 2, false><<<grid, 128, 0, st>>>(a);
       }
     } else {
       expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);

@@ -44,10 +44,16 @@ struct SelectLayout {
 
 // Geometry of the exp-kernel contractions.
 constexpr int kTileRows = 64;   // left rows per workgroup of the 16x16 and fp32 kernels
-constexpr int kTileKeys = 64;   // right rows staged per iteration (chunks are multiples of this)
+constexpr int kTileKeys = 128;  // split chunks are multiples of this (the largest right-row tile)
 
 // Waves per workgroup of the 32x32 bf16 kernel (32 left rows per wave).
-inline int mfma32_waves(int rowsA) { return rowsA > 128 ? 8 : (rowsA > 64 ? 4 : 2); }
+#ifndef WILDCAT_MFMA32_MAXWAVES
+#define WILDCAT_MFMA32_MAXWAVES 8
+#endif
+inline int mfma32_waves(int rowsA) {
+  const int w = rowsA > 128 ? 8 : (rowsA > 64 ? 4 : 2);
+  return w < WILDCAT_MFMA32_MAXWAVES ? w : WILDCAT_MFMA32_MAXWAVES;
+}
 
 // Left rows one workgroup owns, for the kernel that a (d, dtype, rows) call uses.
 inline int contract_rows_per_wg(int d, int rowsA, bool bf16) {
@@ -58,7 +64,8 @@ struct ContractSplit {
   int tiles_a, nsplit, chunk;   // chunk: keys per split, multiple of kTileKeys
   ContractSplit(int U, int r, int n, int rows_per_wg) {
     tiles_a = (r + rows_per_wg - 1) / rows_per_wg;
-    int want = (512 + tiles_a * U - 1) / (tiles_a * U);
+    // about one workgroup per CU (256 CUs) for the large-tile kernels
+    int want = (256 + tiles_a * U - 1) / (tiles_a * U);
     int maxs = (n + kTileKeys - 1) / kTileKeys;
     nsplit = want < 1 ? 1 : (want > maxs ? maxs : want);
     chunk = ((n + nsplit - 1) / nsplit + kTileKeys - 1) / kTileKeys * kTileKeys;
