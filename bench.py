@@ -44,6 +44,34 @@ def contraction_flops(w):
     return c1, c2
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "rpc_round_hbm_traffic_kvcache_n32768_r1024.md")
+
+
+def measured_traffic(w):
+    """HBM bytes of one RPNys round measured with rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (calibrated on a plain 1 GiB elementwise kernel), read from the
+    committed counter summary.  None unless that summary was taken on this
+    workload with the select kernel sources as they are now."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(TRAFFIC_SUMMARY):
+            k, sep, v = line.strip().partition(": ")
+            if sep:
+                fields[k] = v
+        if fields.get("workload") != w.name:
+            return None
+        h = hashlib.sha256()
+        for rel in fields["kernel_sources"].split():
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["kernel_sources_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_round"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, inp, target_s=20.0):
     """The oracle as it stands, timed on host cores on a bounded sample: whole
     kv units (select + weights + attend for their query heads), as many as fit
@@ -81,12 +109,13 @@ def cpu_baseline(w, inp, target_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+                    help="also run one plain elementwise kernel over 1 GiB (1 GiB read + 1 GiB write), "
+                         "the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -150,9 +179,9 @@ def main():
     assert torch.isfinite(O).all().item()
 
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
 
@@ -199,7 +228,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64+bf16" if w.dtype == "bf16" else "f64+fp32",
-        "data": "synthetic (seeded; shapes and statistics of a GQA KV-cache workload)",
+        "data": f"synthetic (seeded '{w.recipe}' recipe with the shapes of the {w.name} workload)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "n": w.n, "m": w.m, "d": w.d, "r": w.r, "beta": w.beta, "input_dtype": w.dtype},
         "phases_ms": {"select": t_sel, "weights": t_wts, "attend": t_att},
@@ -209,13 +238,15 @@ def main():
         "attend_only_rows_per_s": rows / (t_att * 1e-3),
         "exact_attention_gpu": exact,
         "roofline": {
-            "kernel": "one RPNys round over all units: rpc_step (factor/diagonal stream) + rpc_draw (next pivot)",
+            "kernel": "one RPNys round over all units: rpc_step (factor/diagonal stream) + rpc_draw (next pivot) "
+                      "of every unit group, the groups overlapped on their own streams",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(w),
+            "traffic_unit": "bytes per round (rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000)",
             "bytes_per_launch": per_launch_bytes,
             "avg_launch_ms": avg_launch_ms,
         },

@@ -24,8 +24,13 @@
  *    b * kv_heads + h / (q_heads / kv_heads) (contiguous GQA groups).
  *  - The caller allocates and owns every buffer, including the workspace
  *    whose size the *_workspace_bytes queries return.  The library allocates
- *    no device memory and keeps no state between calls; calls are re-entrant
- *    as long as concurrent calls use distinct outputs and workspaces.
+ *    no device memory.  Its only state is, per device, a few auxiliary
+ *    default-priority streams and events that wildcat_select creates on its
+ *    first call and keeps until the process ends: it splits the units into
+ *    groups, forks the groups onto those streams with an event recorded on
+ *    `stream`, and joins them back into `stream` before it returns, so the
+ *    call stays ordered on `stream` like any other.  Calls are re-entrant as
+ *    long as concurrent calls use distinct outputs and workspaces.
  *  - Every call only enqueues kernels on `stream` and returns; results are
  *    ready when the stream is synchronised.  A status is returned at once for
  *    argument, shape, dtype and workspace problems; those are checked on the

@@ -7,7 +7,9 @@
 // before the queries are applied), Lem. 1 paragraph (clip to the column value
 // range), CompressKV / Alg. 2 and WtdAttn / Alg. 3 paragraphs.]
 //
-// Both are one kernel template: a workgroup of NW waves owns 16 rows of the
+// bf16 inputs with d >= 32 run expmm32 (32x32x16 MFMA, described at the
+// kernel); d = 16 runs expmm_bf16, and fp32 inputs run expmm_f32 on the vector
+// ALU.  expmm_bf16: a workgroup of NW waves owns 16 rows of the
 // left operand per wave (fragments kept in registers) and streams the right
 // operand in tiles of 64 rows through LDS.  Per 32 right rows a wave issues
 //   scores^T (16 rows x 16 cols) x2 : v_mfma_f32_16x16x32_bf16 over d

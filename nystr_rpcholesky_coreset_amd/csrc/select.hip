@@ -31,6 +31,7 @@
 // prefix), T is C of the last index, and the pivot is the first l with
 // C_l > u_i T -- the oracle's rule, up to the rounding of the sums.
 #include <climits>
+#include <mutex>
 
 #include "common.hpp"
 #include "layout.hpp"
@@ -51,6 +52,7 @@ struct SelectArgs {
   int32_t* stopped;     // [U]
   int32_t* reff;        // [U]
   int n, npad, nb, r, pbs;
+  int u0;               // first unit of the launch (unit groups, see launch_select_t)
   double c;             // beta / tau^2
 };
 
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void rpc_init(SelectArgs a) {
 template <typename TK, int D, bool RC>
 __global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
   extern __shared__ double smem[];
-  const int u = blockIdx.x;
+  const int u = a.u0 + blockIdx.x;
   if (a.stopped[u]) return;
   draw_and_stage<TK, D, RC>(a, u, i, i == 0, smem);
 }
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(Sele
   double* s_pf = s_kbar + D;             // [4][RB] factor partials
   double* s_pk = s_pf + 4 * RB;          // [4][RB] key partials
   double* s_prow = s_pk + 4 * RB;        // r
-  const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+  const int u = a.u0 + blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
   const int wave = t / kWave, lane = t & (kWave - 1);
   if (a.stopped[u]) return;
   const double* pb = a.pivbuf + ((size_t)u * 2 + (i & 1)) * a.pbs;
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(Sele
 
 // r_eff, -1 padding of S and zero rows of L past r_eff.
 __global__ __launch_bounds__(kBlock) void rpc_finalize(SelectArgs a, int32_t* r_eff_out) {
-  const int u = blockIdx.x, t = threadIdx.x;
+  const int u = a.u0 + blockIdx.x, t = threadIdx.x;
   const int re = a.stopped[u] ? a.reff[u] : a.r;
   if (t == 0) r_eff_out[u] = re;
   for (int j = re + t; j < a.r; j += kBlock) a.S[(size_t)u * a.r + j] = -1;
@@ -479,6 +481,48 @@ __global__ __launch_bounds__(kBlock) void rpc_finalize(SelectArgs a, int32_t* r_
   const size_t from = (size_t)re * a.r, to = (size_t)a.r * a.r;
   for (size_t e = from + t; e < to; e += kBlock) Lu[e] = 0.0;
 }
+
+// Units are independent, so they are split into contiguous groups that run
+// their rounds on separate streams (the caller's stream and auxiliary ones,
+// forked and joined with events): while one group draws its next pivot (one
+// small workgroup per unit) or drains the tail of its streaming launch, the
+// other group's factor stream keeps HBM busy.
+#ifndef WILDCAT_SELECT_GROUPS
+#define WILDCAT_SELECT_GROUPS 4
+#endif
+constexpr int kMaxGroups = 4;
+constexpr int kMaxDevices = 64;
+static_assert(WILDCAT_SELECT_GROUPS >= 1 && WILDCAT_SELECT_GROUPS <= kMaxGroups, "unit groups");
+
+namespace {
+struct AuxStreams {
+  bool ready = false;
+  hipStream_t s[kMaxGroups - 1] = {};
+  hipEvent_t fork = nullptr, join[kMaxGroups - 1] = {};
+};
+std::mutex g_aux_mu;
+AuxStreams g_aux[kMaxDevices];
+
+// Auxiliary streams and events of the current device, created on first use
+// (default priority, non-blocking).  Called with g_aux_mu held.
+hipError_t aux_streams(AuxStreams** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  AuxStreams& x = g_aux[dev];
+  if (!x.ready) {
+    if ((e = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    for (int g = 0; g < kMaxGroups - 1; ++g) {
+      if ((e = hipStreamCreateWithFlags(&x.s[g], hipStreamNonBlocking)) != hipSuccess) return e;
+      if ((e = hipEventCreateWithFlags(&x.join[g], hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    x.ready = true;
+  }
+  *out = &x;
+  return hipSuccess;
+}
+}  // namespace
 
 template <typename TK, int D, bool RC>
 static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hipStream_t st) {
@@ -489,13 +533,43 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
   const size_t lds_draw = (32 + D) * sizeof(double);
   const size_t lds_step = (32 + 2 * D + 8 * RB + a.r) * sizeof(double);
   rpc_init<TK, D, RC><<<grid, kBlock, lds_init, st>>>(a);
-  rpc_draw<TK, D, RC><<<U, kBlock, lds_draw, st>>>(a, 0);
-  for (int i = 0; i < a.r; ++i) {
-    rpc_step<TK, D, RC, WILDCAT_SELECT_NT != 0><<<grid, kBlock, lds_step, st>>>(a, i);
-    if (i + 1 < a.r) rpc_draw<TK, D, RC><<<U, kBlock, lds_draw, st>>>(a, i + 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int G = U < WILDCAT_SELECT_GROUPS ? U : WILDCAT_SELECT_GROUPS;
+  std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
+  hipStream_t gs[kMaxGroups] = {st};
+  SelectArgs ga[kMaxGroups];
+  int gU[kMaxGroups];
+  AuxStreams* aux = nullptr;
+  if (G > 1) {
+    lock.lock();
+    if ((e = aux_streams(&aux)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->fork, st)) != hipSuccess) return e;
+    for (int g = 1; g < G; ++g) {
+      gs[g] = aux->s[g - 1];
+      if ((e = hipStreamWaitEvent(gs[g], aux->fork, 0)) != hipSuccess) return e;
+    }
   }
-  rpc_finalize<<<U, kBlock, 0, st>>>(a, r_eff);
-  return hipGetLastError();
+  for (int g = 0; g < G; ++g) {
+    ga[g] = a;
+    ga[g].u0 = (int)((int64_t)U * g / G);
+    gU[g] = (int)((int64_t)U * (g + 1) / G) - ga[g].u0;
+  }
+  for (int g = 0; g < G; ++g) rpc_draw<TK, D, RC><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], 0);
+  for (int i = 0; i < a.r; ++i) {
+    for (int g = 0; g < G; ++g) {
+      rpc_step<TK, D, RC, WILDCAT_SELECT_NT != 0><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
+      if (i + 1 < a.r) rpc_draw<TK, D, RC><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], i + 1);
+    }
+  }
+  for (int g = 0; g < G; ++g) rpc_finalize<<<gU[g], kBlock, 0, gs[g]>>>(ga[g], r_eff);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int g = 1; g < G; ++g) {
+    if ((e = hipEventRecord(aux->join[g - 1], gs[g])) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, aux->join[g - 1], 0)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename TK, int D>
@@ -530,7 +604,7 @@ hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int rec
   a.kbar = reinterpret_cast<double*>(w + lay.kbar);
   a.stopped = reinterpret_cast<int32_t*>(w + lay.stopped);
   a.reff = reinterpret_cast<int32_t*>(w + lay.reff);
-  a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.c = c;
+  a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.u0 = 0; a.c = c;
   return bf16 ? launch_select_d<bf16_t>(a, U, d, recentre != 0, r_eff, st)
               : launch_select_d<float>(a, U, d, recentre != 0, r_eff, st);
 }

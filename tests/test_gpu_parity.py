@@ -156,3 +156,25 @@ def test_repeat_calls_are_bitwise_deterministic():
     a, b = _run_gpu(inp), _run_gpu(inp)
     for k in ("S", "r_eff", "L", "X", "O"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_mixed_early_stop_across_unit_groups():
+    """Five units run as separate unit groups; units 1 and 3 hold only three
+    distinct keys and stop at r_eff = 3 while the others run all r steps."""
+    rng = np.random.default_rng(11)
+    n, d, r, H = 700, 32, 24, 5
+    K = rng.standard_normal((H, n, d)) / 3
+    for h in (1, 3):
+        base = rng.standard_normal((3, d)) / 3
+        K[h] = base[rng.integers(0, 3, n)]
+        K[h, :3] = base
+    V = rng.standard_normal((H, n, d))
+    Q = rng.standard_normal((H, 48, d)) / 3
+    w = I.Workload("groups", "unit_ball", 1, H, H, 48, n, d, r, 0.5, "fp32", 0)
+    inp = {"Q": Q.astype(np.float32)[None], "K": K.astype(np.float32)[None], "V": V.astype(np.float32)[None],
+           "u": np.random.default_rng(12).random((H, r)), "workload": w}
+    g = _run_gpu(inp)
+    ref = oracle_units(inp, list(range(H)))
+    assert [ref[h].sel.r_eff for h in range(H)] == [r, 3, r, 3, r]
+    for h in range(H):
+        _compare_unit(inp, g, h, ref[h])
