@@ -218,8 +218,12 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
     if (g == 0 && arow < p.rowsA) Y[(size_t)arow * (D + 1) + D] = eacc;
   } else {
     float* O = p.out + (size_t)unit * p.rowsA * D;
-    const float* vmn = p.vmin + (size_t)unitB * D;
-    const float* vmx = p.vmax + (size_t)unitB * D;
+    float lo[CT], hi[CT];   // read once: O stores could alias them
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      lo[ct] = p.vmin[(size_t)unitB * D + 16 * ct + r16];
+      hi[ct] = p.vmax[(size_t)unitB * D + 16 * ct + r16];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rl = 4 * g + i;
@@ -228,9 +232,8 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
       if (row < p.rowsA) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const int c = 16 * ct + r16;
           const float x = oacc[ct][i] / e;
-          O[(size_t)row * D + c] = fminf(fmaxf(x, vmn[c]), vmx[c]);
+          O[(size_t)row * D + 16 * ct + r16] = fminf(fmaxf(x, lo[ct]), hi[ct]);
         }
       }
     }
@@ -246,45 +249,89 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // value MFMA.
 __device__ __forceinline__ int perm32(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// Same contraction with v_mfma_f32_32x32x16_bf16: each wave owns 32 left rows,
-// NWAVE waves share double-buffered LDS tiles of KT right rows (loaded into
-// registers one tile ahead, one barrier per tile; KT = 16 * NWAVE, so the
-// 8-wave configuration uses 139 KiB of the 160 KiB LDS and one tile of MFMA
-// work covers the next tile's load latency).  Per 32 right rows a wave issues
-// D/16 score MFMAs and 2*D/32 value MFMAs.  d >= 32.
-template <int D, int MODE, int NWAVE, bool RC>
-__global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
-  constexpr int NTH = 64 * NWAVE;
+// Same contraction with v_mfma_f32_32x32x16_bf16: each wave owns 32 left rows.
+// KS = 1: NWAVE waves share double-buffered LDS tiles of KT right rows
+// (loaded into registers one tile ahead, one barrier per tile; KT = 16 NWAVE,
+// so the 8-wave configuration uses 139 KiB of the 160 KiB LDS and one tile of
+// MFMA work covers the next tile's load latency).  KS > 1 (attend with few
+// query rows): the right rows are split into KS contiguous ranges, each taken
+// by RW = NWAVE / KS waves (RW row blocks) that stage their own 32-row tiles
+// in a private LDS region.  With RW = 1 the region is single-buffered and
+// the loop has no barrier (a wave's LDS accesses execute in order); with
+// RW = 2 it is double-buffered as for KS = 1 (all ranges run the same number
+// of tiles, so the barrier is shared).  The KS partial sums meet in LDS and
+// are added in a fixed order.  Per 32 right rows a wave issues D/16 score
+// MFMAs and 2*D/32 value MFMAs.  d >= 32.
 #ifndef WILDCAT_MFMA32_KTMAX
 #define WILDCAT_MFMA32_KTMAX 128
 #endif
-  constexpr int KT = (16 * NWAVE < WILDCAT_MFMA32_KTMAX) ? 16 * NWAVE : WILDCAT_MFMA32_KTMAX;   // right rows per tile
-  constexpr int KP = D + 8;                // bf16 pitch of a right row in LDS
-  constexpr int VP = KT + 8;               // bf16 pitch of a transposed value row
+#ifndef WILDCAT_MFMA32_SCHEDBAR
+#define WILDCAT_MFMA32_SCHEDBAR 0   // scheduling barrier before staging also in the shared-tile form
+#endif
+template <int D, int MODE, int NWAVE, bool RC, int KS>
+struct Mfma32Cfg {
+  static constexpr int RW = NWAVE / KS;                 // waves sharing one tile (same right rows)
+  static_assert(RW * KS == NWAVE, "waves = row blocks x key ranges");
+  static constexpr int NTH = 64 * RW;                   // threads staging one tile
+  static constexpr int KT = KS > 1 ? 32 : ((16 * NWAVE < WILDCAT_MFMA32_KTMAX) ? 16 * NWAVE : WILDCAT_MFMA32_KTMAX);
+  static constexpr int NBUF = (KS > 1 && RW == 1) ? 1 : 2;
+  static constexpr int KP = D + 8;                      // bf16 pitch of a right row in LDS
+  static constexpr int VP = KT + 8;                     // bf16 pitch of a transposed value row
+  static constexpr int CT = D / 32;
+  static constexpr size_t B_BYTES = (size_t)KT * KP * 2, VT_BYTES = (size_t)D * VP * 2, E_BYTES = (size_t)KT * 4;
+  static constexpr size_t BUF_BYTES = B_BYTES + VT_BYTES + 2 * E_BYTES;   // keys, values^T, w, offsets
+  static constexpr size_t TILE_BYTES = (size_t)KS * NBUF * BUF_BYTES;
+  static constexpr size_t RED_BYTES = KS > 1 ? (size_t)NWAVE * 64 * (16 * CT + 1) * 4 : 0;
+  static constexpr size_t LDS_BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+};
+
+template <int D, int MODE, int NWAVE, bool RC, int KS>
+__global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
+  using Cfg = Mfma32Cfg<D, MODE, NWAVE, RC, KS>;
+  constexpr int NTH = Cfg::NTH, KT = Cfg::KT, KP = Cfg::KP, VP = Cfg::VP, CT = Cfg::CT;
   constexpr int DK = D / 16;
-  constexpr int CT = D / 32;
   constexpr int KI = KT * (D / 8);         // 16-byte right-row items per tile
-  constexpr int VI = (KT / 2) * (D / 8);   // value items: (row pair, 8 columns)
+  // Value items: weights (bf16 V) (row pair, 8 columns), one 16-byte load per
+  // row; attend (fp32 X, rows of d + 1 values, not 16-byte aligned) (row
+  // pair, 1 column) with the column fastest across lanes, so each 4-byte load
+  // instruction reads consecutive values of one row.
+  constexpr int VI = MODE == kModeWeights ? (KT / 2) * (D / 8) : (KT / 2) * D;
   constexpr int KIPT = (KI + NTH - 1) / NTH;
   constexpr int VIPT = (VI + NTH - 1) / NTH;
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][KT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sVT[2][D * VP];
-  __shared__ __attribute__((aligned(16))) float sE[2][KT];   // attend: w of each right row
-  __shared__ __attribute__((aligned(16))) float sC[2][KT];   // weights with recentring: per-key offsets
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = KS > 1 ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
   const int g2 = lane >> 5, r32 = lane & 31;
+  const int rw = wave % Cfg::RW;                    // row block of the wave
+  const int ks = wave / Cfg::RW;                    // key range of the wave
+  const int gt = t - ks * NTH;                      // thread index among those staging one tile
+  char* const my_lds = lds + (size_t)ks * Cfg::NBUF * Cfg::BUF_BYTES;
+  auto sB = [&](int b) { return reinterpret_cast<uint16_t*>(my_lds + b * Cfg::BUF_BYTES); };
+  auto sVT = [&](int b) { return reinterpret_cast<uint16_t*>(my_lds + b * Cfg::BUF_BYTES + Cfg::B_BYTES); };
+  auto sE = [&](int b) { return reinterpret_cast<float*>(my_lds + b * Cfg::BUF_BYTES + Cfg::B_BYTES + Cfg::VT_BYTES); };
+  auto sC = [&](int b) {
+    return reinterpret_cast<float*>(my_lds + b * Cfg::BUF_BYTES + Cfg::B_BYTES + Cfg::VT_BYTES + Cfg::E_BYTES);
+  };
   const int unit = blockIdx.z, unitB = unit / p.group;
-  const int a0 = blockIdx.y * 32 * NWAVE;
+  const int a0 = blockIdx.y * 32 * Cfg::RW;
   const int split = blockIdx.x;
-  const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
-  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
+  int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  int ntiles = (b_end - b_begin + KT - 1) / KT;
+  if (KS > 1) {
+    // Equal ranges of whole 32-row blocks; every wave runs the same number of
+    // tiles (a range past the end is all masked).
+    const int per = ((p.rowsB + KS - 1) / KS + KT - 1) / KT * KT;
+    b_begin = ks * per;
+    b_end = min(p.rowsB, b_begin + per);
+    ntiles = per / KT;
+  }
   const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (size_t)unit * p.rowsA * D;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (size_t)unitB * p.rowsB * D;
 
   // Left-row fragments (B operand of the score MFMA): row a0 + 32 wave + r32,
   // d = 16 dk + 8 g2 .. +7.
-  const int arow = a0 + wave * 32 + r32;
+  const int arow = a0 + rw * 32 + r32;
   bf16x8 afrag[DK];
 #pragma unroll
   for (int dk = 0; dk < DK; ++dk) {
@@ -301,20 +348,20 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   // store_tile after the compute, so the loads overlap one tile of MFMA work.
   // Prefetch registers as vector values (never stack arrays).
   typedef uint32_t kvec_t __attribute__((ext_vector_type(4 * KIPT)));
-  typedef uint32_t vvec_t __attribute__((ext_vector_type(8 * VIPT)));
-  typedef float xvec_t __attribute__((ext_vector_type(16 * VIPT)));
+  typedef uint32_t vvec_t __attribute__((ext_vector_type(MODE == kModeWeights ? 8 * VIPT : 1)));
+  typedef float xvec_t __attribute__((ext_vector_type(MODE == kModeAttend ? 2 * VIPT : 1)));
   kvec_t kreg = {};           // right-row tile: 16 bytes per item
   vvec_t vreg = {};           // weights: rows 2rp and 2rp+1, 8 bf16 columns each
-  xvec_t xreg = {};           // attend: the same 2 x 8 values of X in fp32
+  xvec_t xreg = {};           // attend: X[2rp][c] and X[2rp+1][c] in fp32
   float ereg = 0.0f, creg = 0.0f;
   // Rows past b_end are read from the last valid row instead (no branches
   // around the loads): their probabilities are masked to 0, so only
   // finiteness matters.
   auto load_tile = [&](int b0) __attribute__((always_inline)) {
-    const int blast = b_end - 1;
+    const int blast = max(min(b_end, p.rowsB) - 1, 0);
 #pragma unroll
     for (int q = 0; q < KIPT; ++q) {
-      const int it = t + q * NTH;
+      const int it = gt + q * NTH;
       if (KI % NTH == 0 || it < KI) {
         const int row = it / (D / 8), c8 = it % (D / 8);
         const int b = min(b0 + row, blast);
@@ -324,11 +371,11 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     }
 #pragma unroll
     for (int q = 0; q < VIPT; ++q) {
-      const int it = t + q * NTH;
+      const int it = gt + q * NTH;
       if (VI % NTH == 0 || it < VI) {
-        const int rp = it % (KT / 2), c8 = it / (KT / 2);
-        const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
-        if (MODE == kModeWeights) {
+        if constexpr (MODE == kModeWeights) {
+          const int rp = it % (KT / 2), c8 = it / (KT / 2);
+          const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
           const uint16_t* V = reinterpret_cast<const uint16_t*>(p.Vs) + (size_t)unitB * p.rowsB * D;
           const uint4 x = *reinterpret_cast<const uint4*>(V + (size_t)b * D + 8 * c8);
           const uint4 y = *reinterpret_cast<const uint4*>(V + (size_t)b1 * D + 8 * c8);
@@ -336,16 +383,18 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
           vreg[8 * q + 4] = y.x; vreg[8 * q + 5] = y.y; vreg[8 * q + 6] = y.z; vreg[8 * q + 7] = y.w;
         } else {
           const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            xreg[16 * q + j] = X[(size_t)b * (D + 1) + 8 * c8 + j];
-            xreg[16 * q + 8 + j] = X[(size_t)b1 * (D + 1) + 8 * c8 + j];
-          }
+          // With d >= 64 every lane of a wave reads the same row pair: the
+          // row is computed once per wave (scalar), the lane adds its column.
+          const int itw = D >= 64 ? __builtin_amdgcn_readfirstlane((gt & ~63) + q * NTH) : it;
+          const int c = D >= 64 ? itw % D + lane : it % D, rp = itw / D;
+          const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
+          xreg[2 * q] = X[(size_t)b * (D + 1) + c];
+          xreg[2 * q + 1] = X[(size_t)b1 * (D + 1) + c];
         }
       }
     }
-    if (t < KT) {
-      const int b = min(b0 + t, blast);
+    if (gt < KT) {
+      const int b = min(b0 + gt, blast);
       if (MODE == kModeAttend) {
         const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
         ereg = X[(size_t)b * (D + 1) + D];
@@ -356,20 +405,20 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < KIPT; ++q) {
-      const int it = t + q * NTH;
+      const int it = gt + q * NTH;
       if (KI % NTH == 0 || it < KI) {
         const int row = it / (D / 8), c8 = it % (D / 8);
-        *reinterpret_cast<uint4*>(&sB[buf][perm32(row) * KP + 8 * c8]) =
+        *reinterpret_cast<uint4*>(&sB(buf)[perm32(row) * KP + 8 * c8]) =
             make_uint4(kreg[4 * q], kreg[4 * q + 1], kreg[4 * q + 2], kreg[4 * q + 3]);
       }
     }
 #pragma unroll
     for (int q = 0; q < VIPT; ++q) {
-      const int it = t + q * NTH;
+      const int it = gt + q * NTH;
       if (VI % NTH == 0 || it < VI) {
-        const int rp = it % (KT / 2), c8 = it / (KT / 2);
-        uint32_t w[8];
-        if (MODE == kModeWeights) {
+        if constexpr (MODE == kModeWeights) {
+          const int rp = it % (KT / 2), c8 = it / (KT / 2);
+          uint32_t w[8];
           const uint32_t xs[4] = {vreg[8 * q], vreg[8 * q + 1], vreg[8 * q + 2], vreg[8 * q + 3]};
           const uint32_t ys[4] = {vreg[8 * q + 4], vreg[8 * q + 5], vreg[8 * q + 6], vreg[8 * q + 7]};
 #pragma unroll
@@ -377,19 +426,19 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
             w[2 * j] = (xs[j] & 0xFFFFu) | (ys[j] << 16);
             w[2 * j + 1] = (xs[j] >> 16) | (ys[j] & 0xFFFF0000u);
           }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(&sVT(buf)[(8 * c8 + j) * VP + 2 * rp]) = w[j];
         } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            w[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[16 * q + j]) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[16 * q + 8 + j]) << 16);
+          const int c = it % D, rp = it / D;
+          *reinterpret_cast<uint32_t*>(&sVT(buf)[c * VP + 2 * rp]) =
+              (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[2 * q]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[2 * q + 1]) << 16);
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(&sVT[buf][(8 * c8 + j) * VP + 2 * rp]) = w[j];
       }
     }
-    if (t < KT) {
-      if (MODE == kModeAttend) sE[buf][t] = ereg;
-      if (RC) sC[buf][t] = creg * kLog2e;
+    if (gt < KT) {
+      if (MODE == kModeAttend) sE(buf)[gt] = ereg;
+      if (RC) sC(buf)[gt] = creg * kLog2e;
     }
   };
 
@@ -407,7 +456,7 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     f32x16 acc = {};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sB[bf][(kofs + r32) * KP + 16 * dk + 8 * g2]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&sB(bf)[(kofs + r32) * KP + 16 * dk + 8 * g2]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), afrag[dk], acc, 0, 0, 0);
     }
     return acc;
@@ -420,8 +469,8 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     if (MODE == kModeAttend) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float4 e0 = *reinterpret_cast<const float4*>(&sE[bf][kofs + 16 * kb + 8 * g2]);
-        const float4 e1 = *reinterpret_cast<const float4*>(&sE[bf][kofs + 16 * kb + 8 * g2 + 4]);
+        const float4 e0 = *reinterpret_cast<const float4*>(&sE(bf)[kofs + 16 * kb + 8 * g2]);
+        const float4 e1 = *reinterpret_cast<const float4*>(&sE(bf)[kofs + 16 * kb + 8 * g2 + 4]);
         ev[8 * kb + 0] = e0.x; ev[8 * kb + 1] = e0.y; ev[8 * kb + 2] = e0.z; ev[8 * kb + 3] = e0.w;
         ev[8 * kb + 4] = e1.x; ev[8 * kb + 5] = e1.y; ev[8 * kb + 6] = e1.z; ev[8 * kb + 7] = e1.w;
       }
@@ -429,8 +478,8 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     if (RC) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float4 c0 = *reinterpret_cast<const float4*>(&sC[bf][kofs + 16 * kb + 8 * g2]);
-        const float4 c1 = *reinterpret_cast<const float4*>(&sC[bf][kofs + 16 * kb + 8 * g2 + 4]);
+        const float4 c0 = *reinterpret_cast<const float4*>(&sC(bf)[kofs + 16 * kb + 8 * g2]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&sC(bf)[kofs + 16 * kb + 8 * g2 + 4]);
         cv[8 * kb + 0] = c0.x; cv[8 * kb + 1] = c0.y; cv[8 * kb + 2] = c0.z; cv[8 * kb + 3] = c0.w;
         cv[8 * kb + 4] = c1.x; cv[8 * kb + 5] = c1.y; cv[8 * kb + 6] = c1.z; cv[8 * kb + 7] = c1.w;
       }
@@ -452,52 +501,90 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sVT[bf][(32 * ct + r32) * VP + kofs + 16 * kb + 8 * g2]);
+        const uint4 v = *reinterpret_cast<const uint4*>(&sVT(bf)[(32 * ct + r32) * VP + kofs + 16 * kb + 8 * g2]);
         oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pfrag[kb], __builtin_bit_cast(bf16x8, v), oacc[ct], 0, 0, 0);
       }
     }
   };
 
-  if (b_begin < b_end) {
+  if (ntiles > 0) {
     load_tile(b_begin);
     store_tile(0);
   }
   __syncthreads();
   int buf = 0;
-  for (int b0 = b_begin; b0 < b_end; b0 += KT) {
+  for (int it = 0; it < ntiles; ++it) {
+    const int b0 = b_begin + it * KT;
     // Unconditional prefetch (the last tile re-loads itself into the idle
     // buffer): keeps the loads out of branches so they stay in flight.
-    const int bnext = b0 + KT < b_end ? b0 + KT : b0;
+    const int bnext = it + 1 < ntiles ? b0 + KT : b0;
     load_tile(bnext);
 
     // Software pipeline over the tile's 32-row blocks: the score MFMAs of
     // block k+1 are issued before the probabilities of block k are computed,
     // so the VALU work co-executes with the matrix core.
-    f32x16 s_next = scores(buf, 0);
+    // (Not in the key-split form: there the loads dominate and the second
+    // score tile's registers are needed for the prefetch.)
+    constexpr bool PIPE = KS == 1;
+    f32x16 s_next = {};
+    if (PIPE) s_next = scores(buf, 0);
     const bool full_tile = b0 + KT <= b_end;
 #pragma unroll
     for (int kb32 = 0; kb32 < KT / 32; ++kb32) {
-      const f32x16 s_cur = s_next;
-      if (kb32 + 1 < KT / 32) s_next = scores(buf, 32 * (kb32 + 1));
+      const f32x16 s_cur = PIPE ? s_next : scores(buf, 32 * kb32);
+      if (PIPE && kb32 + 1 < KT / 32) s_next = scores(buf, 32 * (kb32 + 1));
       bf16x8 pfrag[2];
       if (full_tile) probs(std::false_type{}, s_cur, buf, 32 * kb32, b0, pfrag);
       else probs(std::true_type{}, s_cur, buf, 32 * kb32, b0, pfrag);
       values(buf, 32 * kb32, pfrag);
     }
-    store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    // Keep the staging of the next tile (which waits for its loads) after
+    // this tile's MFMAs: without the barrier the scheduler interleaves the
+    // two and every tile waits for its successor's loads.
+    if (KS > 1 || WILDCAT_MFMA32_SCHEDBAR) __builtin_amdgcn_sched_barrier(0);
+    if (Cfg::NBUF == 1) {
+      // Private single buffer: the wave's own reads of this tile were issued
+      // before these stores, and one wave's LDS accesses execute in order.
+      store_tile(0);
+    } else {
+      store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   // eacc: partial over this lane's half of the keys -> full sum for row r32.
   eacc += __shfl_xor(eacc, 32, 64);
+  if (KS > 1) {
+    // Partial sums of the KS key ranges, [wave][value][lane], then added in
+    // the order ks = 0, 1, ..., KS-1 by the waves of range 0.
+    constexpr int NV = 16 * CT + 1;
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((size_t)wave * NV + 16 * ct + v) * 64 + lane] = oacc[ct][v];
+    red[((size_t)wave * NV + 16 * CT) * 64 + lane] = eacc;
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll 1
+    for (int q = 1; q < KS; ++q) {
+      const size_t w2 = (size_t)q * Cfg::RW + rw;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[ct][v] += red[(w2 * NV + 16 * ct + v) * 64 + lane];
+      eacc += red[(w2 * NV + 16 * CT) * 64 + lane];
+    }
+  }
   // oacc[ct][v] = result for left row 8 (v/4) + 4 g2 + v % 4 (of the wave's 32),
   // column 32 ct + r32.
   if (MODE == kModeWeights) {
     float* Y = p.out + ((size_t)split * p.units + unit) * p.rowsA * (D + 1);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = a0 + wave * 32 + 8 * (v >> 2) + 4 * g2 + (v & 3);
+      const int row = a0 + rw * 32 + 8 * (v >> 2) + 4 * g2 + (v & 3);
       if (row < p.rowsA) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) Y[(size_t)row * (D + 1) + 32 * ct + r32] = oacc[ct][v];
@@ -506,19 +593,23 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     if (g2 == 0 && arow < p.rowsA) Y[(size_t)arow * (D + 1) + D] = eacc;
   } else {
     float* O = p.out + (size_t)unit * p.rowsA * D;
-    const float* vmn = p.vmin + (size_t)unitB * D;
-    const float* vmx = p.vmax + (size_t)unitB * D;
+    // The lane's column bounds, read once (O stores could alias them, so
+    // reading inside the store loop would reload them after every store).
+    float lo[CT], hi[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      lo[ct] = p.vmin[(size_t)unitB * D + 32 * ct + r32];
+      hi[ct] = p.vmax[(size_t)unitB * D + 32 * ct + r32];
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int rl = 8 * (v >> 2) + 4 * g2 + (v & 3);
       const float e = __shfl(eacc, rl, 64);
-      const int row = a0 + wave * 32 + rl;
+      const int row = a0 + rw * 32 + rl;
       if (row < p.rowsA) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int c = 32 * ct + r32;
-          O[(size_t)row * D + c] = fminf(fmaxf(oacc[ct][v] / e, vmn[c]), vmx[c]);
-        }
+        for (int ct = 0; ct < CT; ++ct)
+          O[(size_t)row * D + 32 * ct + r32] = fminf(fmaxf(oacc[ct][v] / e, lo[ct]), hi[ct]);
       }
     }
   }
@@ -602,12 +693,17 @@ __global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
     if (row < p.rowsA) {
       const float e = sN[rl];
       float* O = p.out + ((size_t)unit * p.rowsA + row) * D;
-      const float* vmn = p.vmin + (size_t)unitB * D;
-      const float* vmx = p.vmax + (size_t)unitB * D;
+      float lo[NC], hi[NC];   // read before any store: O stores could alias them
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = qc + 4 * j;
-        if (c < D) O[c] = fminf(fmaxf(acc[j] / e, vmn[c]), vmx[c]);
+        lo[j] = c < D ? p.vmin[(size_t)unitB * D + c] : 0.0f;
+        hi[j] = c < D ? p.vmax[(size_t)unitB * D + c] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = qc + 4 * j;
+        if (c < D) O[c] = fminf(fmaxf(acc[j] / e, lo[j]), hi[j]);
       }
     }
   }
@@ -734,13 +830,37 @@ __global__ __launch_bounds__(kBlock) void value_range_final(const float* part, f
 }
 
 // ---------------------------------------------------------------- host side
+// Key split of the bf16 attend contraction (d >= 32): when the query row
+// tiles alone give fewer than 256 workgroups (few query rows per head), a
+// workgroup takes 32 query rows and its waves split the pivots into 8 ranges
+// (d <= 64) or 4 ranges (d = 128), one wave per range.  Returns the number
+// of ranges, 1 for no split.
+inline int attend_key_split(int Uq, int m, int r, int d, bool bf16) {
+  if (!bf16 || d < 32) return 1;
+  const int rows = contract_rows_per_wg(d, m, true);
+  const long wgs = (long)Uq * ((m + rows - 1) / rows);
+  return (wgs < 256 && r >= 8 * 32) ? (d >= 128 ? 4 : 8) : 1;
+}
+
 // Grid: x = splits of the right rows, y = tiles of left rows, z = units.
 // bf16 with d >= 32 runs the 32x32x16 kernel with 2, 4 or 8 waves (32 left
-// rows each, see mfma32_waves); bf16 d = 16 the 16x16x32 kernel; fp32 the
-// vector-ALU kernel.  contract_rows_per_wg gives the same tiling to the
-// workspace layout.
+// rows each, see mfma32_waves), or for attend with few query rows the
+// 8-wave key-split form (attend_key_split); bf16 d = 16 the 16x16x32 kernel;
+// fp32 the vector-ALU kernel.  contract_rows_per_wg gives the same tiling to
+// the workspace layout.
 template <int D, int MODE>
 static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream_t st) {
+  if constexpr (D >= 32 && MODE == kModeAttend) {
+    const int ks = bf16 ? attend_key_split(a.units, a.rowsA, a.rowsB, D, true) : 1;
+    if (ks > 1) {
+      // One wave per key range, 32 query rows per workgroup.  d = 128 uses 4
+      // waves: its staging registers need more than the 256 per lane that an
+      // 8-wave workgroup allows.
+      constexpr int KS = D >= 128 ? 4 : 8;
+      expmm32<D, MODE, KS, false, KS><<<dim3(1, (a.rowsA + 31) / 32, a.units), 64 * KS, 0, st>>>(a);
+      return;
+    }
+  }
   const int rows = contract_rows_per_wg(D, a.rowsA, bf16);
   const dim3 grid(nsplit, (a.rowsA + rows - 1) / rows, a.units);
   if (bf16) {
@@ -748,13 +868,13 @@ static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream
       const int nw = mfma32_waves(a.rowsA);
       if (MODE == kModeWeights && a.colc != nullptr) {   // recentring offsets (weights only)
         constexpr bool RC = MODE == kModeWeights;
-        if (nw == 8) expmm32<D, MODE, 8, RC><<<grid, 512, 0, st>>>(a);
-        else if (nw == 4) expmm32<D, MODE, 4, RC><<<grid, 256, 0, st>>>(a);
-        else expmm32<D, MODE, 2, RC><<<grid, 128, 0, st>>>(a);
+        if (nw == 8) expmm32<D, MODE, 8, RC, 1><<<grid, 512, 0, st>>>(a);
+        else if (nw == 4) expmm32<D, MODE, 4, RC, 1><<<grid, 256, 0, st>>>(a);
+        else expmm32<D, MODE, 2, RC, 1><<<grid, 128, 0, st>>>(a);
       } else {
-        if (nw == 8) expmm32<D, MODE, 8, false><<<grid, 512, 0, st>>>(a);
-        else if (nw == 4) expmm32<D, MODE, 4, false><<<grid, 256, 0, st>>>(a);
-        else expmm32<D, MODE, 2, false><<<grid, 128, 0, st>>>(a);
+        if (nw == 8) expmm32<D, MODE, 8, false, 1><<<grid, 512, 0, st>>>(a);
+        else if (nw == 4) expmm32<D, MODE, 4, false, 1><<<grid, 256, 0, st>>>(a);
+        else expmm32<D, MODE, 2, false, 1><<<grid, 128, 0, st>>>(a);
       }
     } else {
       expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);

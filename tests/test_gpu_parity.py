@@ -31,6 +31,12 @@ SMALL_CASES = {
     "sphere_h2": I.scaled_workload(C5, q_heads=2, kv_heads=2, n=3000, m=700, r=150),
     "kv_recentre_tau": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=1500, r=100, recentre=True, tau=1.7),
     "probe_recentre": I.scaled_workload(C1, n=700, m=100, r=40, recentre=True, tau=0.8, seed=9),
+    # few query rows and r >= 256: attend splits the pivots over the waves of
+    # a workgroup (d = 128: 4 ranges, the last one ragged; d = 64 and 32: 8
+    # ranges, some past r and empty, ragged query tiles)
+    "kv_keysplit_d128": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=3000, m=64, r=300, seed=21),
+    "latent_keysplit_d64": I.scaled_workload(C3, batch=1, q_heads=2, kv_heads=2, n=2000, m=100, r=280, seed=22),
+    "kv_keysplit_d32": I.scaled_workload(C4, q_heads=4, kv_heads=1, n=1200, m=50, r=260, d=32, seed=23),
 }
 
 
