@@ -20,8 +20,9 @@
 // which is exactly the A-operand layout of the second MFMA: P never leaves the
 // registers.  V is staged transposed in LDS so the second MFMA's B operand is
 // one 16-byte LDS read.  The last column ([.., 1] or w) is accumulated on the
-// vector ALU from the same bf16-rounded P.  No running maximum is needed: the
-// exponents are bounded by the input-range contract.
+// vector ALU (expmm_bf16: from the bf16-rounded P; expmm32: from P in fp32
+// before rounding).  No running maximum is needed: the exponents are bounded
+// by the input-range contract.
 #include <type_traits>
 
 #include "common.hpp"
@@ -462,7 +463,8 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     return acc;
   };
   // Probabilities exp2(scale2 * s + offsets) as bf16 in the value MFMA's
-  // A-operand layout, and the last-column sum from the same rounded values.
+  // A-operand layout, and the last-column sum from the fp32 values before
+  // rounding (no conversion back from bf16 on the vector ALU).
   auto probs = [&](auto masked_tag, const f32x16& sv, int bf, int kofs, int b0, bf16x8 (&pfrag)[2]) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     float ev[16], cv[16];
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
       if (MASKED) pv = (b0 + kofs + 16 * (v >> 3) + 8 * g2 + (v & 7) < b_end) ? pv : 0.0f;
       const __bf16 h = (__bf16)pv;
       pfrag[v >> 3][v & 7] = h;
-      eacc = MODE == kModeAttend ? fmaf((float)h, ev[v], eacc) : eacc + (float)h;
+      eacc = MODE == kModeAttend ? fmaf(pv, ev[v], eacc) : eacc + pv;
     }
   };
   // oacc += P (32 rows x 32 right rows) x V (32 right rows x D).
