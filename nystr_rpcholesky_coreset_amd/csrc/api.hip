@@ -3,7 +3,7 @@
 #include <math.h>
 
 #include "../../include/wildcat.h"
-#include "layout.hpp"
+#include "weights_layout.hpp"
 
 namespace wc {
 hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,

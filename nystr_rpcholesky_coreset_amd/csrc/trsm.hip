@@ -12,11 +12,17 @@
 // publishes the solved values to LDS; then every thread subtracts the tile's
 // contribution from its own remaining rows, with independent coalesced loads
 // (L^T rows in the forward sweep, L rows in the backward sweep: consecutive
-// threads read consecutive doubles).  Y is first summed from the split-n
-// partials of the contraction, in a fixed order, by its own kernel.  Only the
-// first r_eff rows take part; rows past r_eff of X are written as 0.
+// threads read consecutive doubles).  Y is summed from the split-n partials
+// of the contraction, in a fixed order, as the right-hand sides are loaded.
+// Only the first r_eff rows take part; rows past r_eff of X are written as 0.
+//
+// XCD-aware launch: workgroups are dispatched to the 8 XCDs round-robin by
+// linear index, so workgroup b runs on XCD b % 8; all column groups of unit u
+// are given indices with b % 8 == u % 8.  They then share one XCD's L2 and
+// walk the same 64-row panels of L at about the same time, so each panel
+// comes from HBM about once per unit instead of once per column group.
 #include "common.hpp"
-#include "layout.hpp"
+#include "weights_layout.hpp"
 
 namespace wc {
 
@@ -37,15 +43,6 @@ __global__ __launch_bounds__(kBlock) void transpose_l(const double* L, double* L
     const int row = bx + k, col = by + tx;
     if (row < r && col < r) LTu[(size_t)row * r + col] = tile[tx][k];
   }
-}
-
-// Y[u][i][c] = sum over splits of the contraction partials (fp64, split order).
-__global__ __launch_bounds__(kBlock) void reduce_y(const float* ypart, double* Y, int nsplit, size_t per_split) {
-  const size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x;
-  if (e >= per_split) return;
-  double acc = 0.0;
-  for (int s = 0; s < nsplit; ++s) acc += (double)ypart[(size_t)s * per_split + e];
-  Y[e] = acc;
 }
 
 // Broadcast lane k's double to the whole wave (k uniform).
@@ -72,23 +69,52 @@ __device__ __forceinline__ void stage_diag_wide(double* Td, const double* Lu, in
   }
 }
 
+constexpr int kXcds = 8;
+#ifndef WILDCAT_TRSM_XCD
+#define WILDCAT_TRSM_XCD 1   // place all column groups of a unit on one XCD
+#endif
+
 template <int CPW, int RPT>
-__global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const double* Y, const double* L, const double* LT,
-                                                          const int32_t* r_eff, float* X, int r, int D1) {
+__global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, int nsplit, const double* L,
+                                                          const double* LT, const int32_t* r_eff, float* X, int r,
+                                                          int D1, int U, int G) {
   __shared__ double Td[64 * 64];
   __shared__ double Zt[64 * CPW];
-  const int u = blockIdx.y, c0 = blockIdx.x * CPW, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int u = WILDCAT_TRSM_XCD ? (slot / G) * kXcds + xcd : (int)blockIdx.x / G;
+  const int c0 = (WILDCAT_TRSM_XCD ? slot % G : (int)blockIdx.x % G) * CPW;
+  if (u >= U) return;   // whole workgroup
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int re = r_eff[u];
   const double* Lu = L + (size_t)u * r * r;
   const double* LTu = LT + (size_t)u * r * r;
-  const double* Yu = Y + (size_t)u * r * D1;
 
+  // Right-hand sides: Y = sum over the contraction's splits, in split order.
+  const size_t per_split = (size_t)U * r * D1;
+  const float* Yu = ypart + (size_t)u * r * D1;
   double z[RPT][CPW];
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
     const int i = t + q * kTrsmThreads;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) z[q][c] = (i < re && c0 + c < D1) ? Yu[(size_t)i * D1 + c0 + c] : 0.0;
+    for (int c = 0; c < CPW; ++c) z[q][c] = 0.0;
+    if (i < re) {
+      // 4 splits' loads in flight, then added in split order
+      for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
+        float part[4][CPW];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            part[k][c] = (sp0 + k < nsplit && c0 + c < D1)
+                             ? Yu[(size_t)(sp0 + k) * per_split + (size_t)i * D1 + c0 + c] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+            if (sp0 + k < nsplit) z[q][c] += (double)part[k][c];
+      }
+    }
   }
 
   // Forward: L z = y.
@@ -98,22 +124,28 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const double* Y, const
     stage_diag_wide(Td, Lu, r, i0, nt);
     __syncthreads();
     if (wave == wo) {
+      // The owner's rows (slot qo, a uniform branch per slot so that every
+      // index stays constant) are solved in registers with lane broadcasts;
+      // the updates are selects, not branches: the 64 steps are
+      // straight-line code.
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q != qo) continue;
-        const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
-        for (int k = 0; k < nt; ++k) {
-          const double ik = readlane_d(inv, k);
-          const double lik = (lane > k && lane < nt) ? Td[dt_idx(lane, k)] : 0.0;
+        if (q == qo) {
+          const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
+          for (int k = 0; k < nt; ++k) {
+            const double ik = readlane_d(inv, k);
+            const double lik = Td[dt_idx(lane, k)];
+            const bool below = lane > k && lane < nt, diag = lane == k;
 #pragma unroll
-          for (int c = 0; c < CPW; ++c) {
-            const double zk = readlane_d(z[q][c], k) * ik;
-            if (lane == k) z[q][c] = zk;
-            else if (lane > k) z[q][c] = fma(-lik, zk, z[q][c]);
+            for (int c = 0; c < CPW; ++c) {
+              const double zk = readlane_d(z[q][c], k) * ik;
+              const double upd = fma(-lik, zk, z[q][c]);
+              z[q][c] = diag ? zk : (below ? upd : z[q][c]);
+            }
           }
-        }
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
+          for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
+        }
       }
     }
     __syncthreads();
@@ -146,20 +178,22 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const double* Y, const
     if (wave == wo) {
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q != qo) continue;
-        const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
-        for (int k = nt - 1; k >= 0; --k) {
-          const double ik = readlane_d(inv, k);
-          const double lki = (lane < k) ? Td[dt_idx(k, lane)] : 0.0;
+        if (q == qo) {
+          const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
+          for (int k = nt - 1; k >= 0; --k) {
+            const double ik = readlane_d(inv, k);
+            const double lki = Td[dt_idx(k, lane)];
+            const bool above = lane < k, diag = lane == k;
 #pragma unroll
-          for (int c = 0; c < CPW; ++c) {
-            const double xk = readlane_d(z[q][c], k) * ik;
-            if (lane == k) z[q][c] = xk;
-            else if (lane < k) z[q][c] = fma(-lki, xk, z[q][c]);
+            for (int c = 0; c < CPW; ++c) {
+              const double xk = readlane_d(z[q][c], k) * ik;
+              const double upd = fma(-lki, xk, z[q][c]);
+              z[q][c] = diag ? xk : (above ? upd : z[q][c]);
+            }
           }
-        }
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
+          for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
+        }
       }
     }
     __syncthreads();
@@ -196,21 +230,21 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const double* Y, const
 }
 
 template <int CPW, int RPT>
-static void launch_trsm_t(int U, int r, int D1, const double* Y, const double* L, const double* LT,
+static void launch_trsm_t(int U, int r, int D1, const float* ypart, int nsplit, const double* L, const double* LT,
                           const int32_t* r_eff, float* X, hipStream_t st) {
-  trsm_cols<CPW, RPT><<<dim3((D1 + CPW - 1) / CPW, U), kTrsmThreads, 0, st>>>(Y, L, LT, r_eff, X, r, D1);
+  const int G = (D1 + CPW - 1) / CPW;                      // column groups per unit
+  const int slots = (U + kXcds - 1) / kXcds * G;          // workgroups per XCD
+  trsm_cols<CPW, RPT><<<slots * kXcds, kTrsmThreads, 0, st>>>(ypart, nsplit, L, LT, r_eff, X, r, D1, U, G);
 }
 
 // Rows per thread: 1 up to r = 1024, 2 up to 2048, 4 up to 4096.
-hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, double* Y, const double* L, double* LT,
+hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
                        const int32_t* r_eff, float* X, hipStream_t st) {
   const int D1 = d + 1;
-  const size_t per_split = (size_t)U * r * D1;
-  reduce_y<<<(unsigned)((per_split + kBlock - 1) / kBlock), kBlock, 0, st>>>(ypart, Y, nsplit, per_split);
   transpose_l<<<dim3((r + 31) / 32, (r + 31) / 32, U), kBlock, 0, st>>>(L, LT, r);
-  if (r <= 1024) launch_trsm_t<4, 1>(U, r, D1, Y, L, LT, r_eff, X, st);
-  else if (r <= 2048) launch_trsm_t<4, 2>(U, r, D1, Y, L, LT, r_eff, X, st);
-  else launch_trsm_t<4, 4>(U, r, D1, Y, L, LT, r_eff, X, st);
+  if (r <= 1024) launch_trsm_t<4, 1>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  else if (r <= 2048) launch_trsm_t<4, 2>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  else launch_trsm_t<4, 4>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
   return hipGetLastError();
 }
 
