@@ -4,9 +4,9 @@
 // W = h_tau(K_S, K_S)^{-1} h_tau(K_S, K); with h_tau(K_S, K_S) = L L^T from the
 // Cholesky pivot block, W [V, 1] = L^{-T} L^{-1} (h_tau(K_S, K) [V, 1]).]
 //
-// One workgroup of 1024 threads per (unit, group of CPW right-hand-side
-// columns), right-looking by tiles of 64 rows.  Thread t owns rows
-// t, t + 1024, ... of the right-hand sides and keeps them in registers for the
+// One workgroup of NT threads (256 for r <= 256, else 1024) per (unit, group
+// of CPW right-hand-side columns), right-looking by tiles of 64 rows.  Thread
+// t owns rows t, t + NT, ... of the right-hand sides and keeps them in registers for the
 // whole solve, so the 64 rows of a tile belong to exactly one wave: that wave
 // solves the tile's 64x64 triangle (staged in LDS) with lane broadcasts and
 // publishes the solved values to LDS; then every thread subtracts the tile's
@@ -57,14 +57,15 @@ __device__ __forceinline__ double readlane_d(double v, int k) {
 // (forward) and column-wise (backward) lane access are bank-conflict free.
 __device__ __forceinline__ int dt_idx(int a, int b) { return a * 64 + (b ^ a); }
 
-constexpr int kTrsmThreads = 1024;
-
-// Td <- L[i0 .. i0+nt)[i0 .. i0+nt) (zeros outside); waves 0..15 take 4 rows each.
+// Td <- L[i0 .. i0+nt)[i0 .. i0+nt) (zeros outside); each of the NT/64
+// waves takes 64 / (NT/64) rows.
+template <int NT>
 __device__ __forceinline__ void stage_diag_wide(double* Td, const double* Lu, int r, int i0, int nt) {
+  constexpr int RW = 64 / (NT / 64);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int a = w * 4 + q;
+  for (int q = 0; q < RW; ++q) {
+    const int a = w * RW + q;
     Td[dt_idx(a, lane)] = (a < nt && lane < nt) ? Lu[(size_t)(i0 + a) * r + i0 + lane] : 0.0;
   }
 }
@@ -74,8 +75,8 @@ constexpr int kXcds = 8;
 #define WILDCAT_TRSM_XCD 1   // place all column groups of a unit on one XCD
 #endif
 
-template <int CPW, int RPT>
-__global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, int nsplit, const double* L,
+template <int CPW, int RPT, int NT>
+__global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, const double* L,
                                                           const double* LT, const int32_t* r_eff, float* X, int r,
                                                           int D1, int U, int G) {
   __shared__ double Td[64 * 64];
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
   double z[RPT][CPW];
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
-    const int i = t + q * kTrsmThreads;
+    const int i = t + q * NT;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) z[q][c] = 0.0;
     if (i < re) {
@@ -120,8 +121,8 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
   // Forward: L z = y.
   for (int i0 = 0; i0 < re; i0 += 64) {
     const int nt = min(64, re - i0);
-    const int qo = i0 / kTrsmThreads, wo = (i0 % kTrsmThreads) / 64;   // owner slot and wave
-    stage_diag_wide(Td, Lu, r, i0, nt);
+    const int qo = i0 / NT, wo = (i0 % NT) / 64;   // owner slot and wave
+    stage_diag_wide<NT>(Td, Lu, r, i0, nt);
     __syncthreads();
     if (wave == wo) {
       // The owner's rows (slot qo, a uniform branch per slot so that every
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < RPT; ++q) {
-      const int i = t + q * kTrsmThreads;
+      const int i = t + q * NT;
       if (i >= i0 + nt && i < re) {
         double acc[CPW];
 #pragma unroll
@@ -172,8 +173,8 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
   // Backward: L^T x = z.
   for (int i0 = ((re - 1) / 64) * 64; re > 0 && i0 >= 0; i0 -= 64) {
     const int nt = min(64, re - i0);
-    const int qo = i0 / kTrsmThreads, wo = (i0 % kTrsmThreads) / 64;
-    stage_diag_wide(Td, Lu, r, i0, nt);
+    const int qo = i0 / NT, wo = (i0 % NT) / 64;
+    stage_diag_wide<NT>(Td, Lu, r, i0, nt);
     __syncthreads();
     if (wave == wo) {
 #pragma unroll
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < RPT; ++q) {
-      const int i = t + q * kTrsmThreads;
+      const int i = t + q * NT;
       if (i < i0) {
         double acc[CPW];
 #pragma unroll
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
   float* Xu = X + (size_t)u * r * D1;
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
-    const int i = t + q * kTrsmThreads;
+    const int i = t + q * NT;
     if (i < r) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
@@ -229,22 +230,24 @@ __global__ __launch_bounds__(kTrsmThreads) void trsm_cols(const float* ypart, in
   }
 }
 
-template <int CPW, int RPT>
+template <int CPW, int RPT, int NT>
 static void launch_trsm_t(int U, int r, int D1, const float* ypart, int nsplit, const double* L, const double* LT,
                           const int32_t* r_eff, float* X, hipStream_t st) {
   const int G = (D1 + CPW - 1) / CPW;                      // column groups per unit
   const int slots = (U + kXcds - 1) / kXcds * G;          // workgroups per XCD
-  trsm_cols<CPW, RPT><<<slots * kXcds, kTrsmThreads, 0, st>>>(ypart, nsplit, L, LT, r_eff, X, r, D1, U, G);
+  trsm_cols<CPW, RPT, NT><<<slots * kXcds, NT, 0, st>>>(ypart, nsplit, L, LT, r_eff, X, r, D1, U, G);
 }
 
-// Rows per thread: 1 up to r = 1024, 2 up to 2048, 4 up to 4096.
+// Threads and rows per thread: 256 x 1 up to r = 256, 1024 x 1 up to 1024,
+// 1024 x 2 up to 2048, 1024 x 4 up to 4096.
 hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
                        const int32_t* r_eff, float* X, hipStream_t st) {
   const int D1 = d + 1;
   transpose_l<<<dim3((r + 31) / 32, (r + 31) / 32, U), kBlock, 0, st>>>(L, LT, r);
-  if (r <= 1024) launch_trsm_t<4, 1>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
-  else if (r <= 2048) launch_trsm_t<4, 2>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
-  else launch_trsm_t<4, 4>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  if (r <= 256) launch_trsm_t<4, 1, 256>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  else if (r <= 1024) launch_trsm_t<4, 1, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  else if (r <= 2048) launch_trsm_t<4, 2, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  else launch_trsm_t<4, 4, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
   return hipGetLastError();
 }
 
