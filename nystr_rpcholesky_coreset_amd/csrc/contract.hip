@@ -293,10 +293,18 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   constexpr int DK = D / 16;
   constexpr int KI = KT * (D / 8);         // 16-byte right-row items per tile
   // Value items: weights (bf16 V) (row pair, 8 columns), one 16-byte load per
-  // row; attend (fp32 X, rows of d + 1 values, not 16-byte aligned) (row
-  // pair, 1 column) with the column fastest across lanes, so each 4-byte load
-  // instruction reads consecutive values of one row.
-  constexpr int VI = MODE == kModeWeights ? (KT / 2) * (D / 8) : (KT / 2) * D;
+  // row; attend (fp32 X, rows of d + 1 values: 4-byte aligned only) (row
+  // pair, 4 columns), one 16-byte load per row (global memory takes 16-byte
+  // loads at 4-byte alignment), the 64 items of a wave spanning 8 row pairs
+  // x 8 column quads (8 rows of 128 contiguous bytes per load instruction,
+  // at most 2-way bank conflicts on the transposed LDS stores).
+  constexpr int VI = MODE == kModeWeights ? (KT / 2) * (D / 8) : (KT / 2) * (D / 4);
+  static_assert(MODE == kModeWeights || (KT % 16 == 0 && D % 32 == 0), "attend value items: 8 x 8 blocks");
+  auto xitem = [](int it, int& rp, int& c4) __attribute__((always_inline)) {
+    const int blk = it >> 6, w = it & 63;
+    rp = (w & 7) + 8 * (blk / (D / 32));
+    c4 = (w >> 3) + 8 * (blk % (D / 32));
+  };
   constexpr int KIPT = (KI + NTH - 1) / NTH;
   constexpr int VIPT = (VI + NTH - 1) / NTH;
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
@@ -350,10 +358,11 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   // Prefetch registers as vector values (never stack arrays).
   typedef uint32_t kvec_t __attribute__((ext_vector_type(4 * KIPT)));
   typedef uint32_t vvec_t __attribute__((ext_vector_type(MODE == kModeWeights ? 8 * VIPT : 1)));
-  typedef float xvec_t __attribute__((ext_vector_type(MODE == kModeAttend ? 2 * VIPT : 1)));
+  typedef float xvec_t __attribute__((ext_vector_type(MODE == kModeAttend ? 8 * VIPT : 1)));
+  typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
   kvec_t kreg = {};           // right-row tile: 16 bytes per item
   vvec_t vreg = {};           // weights: rows 2rp and 2rp+1, 8 bf16 columns each
-  xvec_t xreg = {};           // attend: X[2rp][c] and X[2rp+1][c] in fp32
+  xvec_t xreg = {};           // attend: X[2rp][4c4 .. +3] and X[2rp+1][4c4 .. +3] in fp32
   float ereg = 0.0f, creg = 0.0f;
   // Rows past b_end are read from the last valid row instead (no branches
   // around the loads): their probabilities are masked to 0, so only
@@ -384,13 +393,13 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
           vreg[8 * q + 4] = y.x; vreg[8 * q + 5] = y.y; vreg[8 * q + 6] = y.z; vreg[8 * q + 7] = y.w;
         } else {
           const float* X = reinterpret_cast<const float*>(p.Vs) + (size_t)unitB * p.rowsB * (D + 1);
-          // With d >= 64 every lane of a wave reads the same row pair: the
-          // row is computed once per wave (scalar), the lane adds its column.
-          const int itw = D >= 64 ? __builtin_amdgcn_readfirstlane((gt & ~63) + q * NTH) : it;
-          const int c = D >= 64 ? itw % D + lane : it % D, rp = itw / D;
+          int rp, c4;
+          xitem(it, rp, c4);
           const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
-          xreg[2 * q] = X[(size_t)b * (D + 1) + c];
-          xreg[2 * q + 1] = X[(size_t)b1 * (D + 1) + c];
+          const f4u x = *reinterpret_cast<const f4u*>(X + (unsigned)(b * (D + 1) + 4 * c4));
+          const f4u y = *reinterpret_cast<const f4u*>(X + (unsigned)(b1 * (D + 1) + 4 * c4));
+          xreg[8 * q] = x.x; xreg[8 * q + 1] = x.y; xreg[8 * q + 2] = x.z; xreg[8 * q + 3] = x.w;
+          xreg[8 * q + 4] = y.x; xreg[8 * q + 5] = y.y; xreg[8 * q + 6] = y.z; xreg[8 * q + 7] = y.w;
         }
       }
     }
@@ -430,10 +439,13 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(&sVT(buf)[(8 * c8 + j) * VP + 2 * rp]) = w[j];
         } else {
-          const int c = it % D, rp = it / D;
-          *reinterpret_cast<uint32_t*>(&sVT(buf)[c * VP + 2 * rp]) =
-              (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[2 * q]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[2 * q + 1]) << 16);
+          int rp, c4;
+          xitem(it, rp, c4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint32_t*>(&sVT(buf)[(4 * c4 + j) * VP + 2 * rp]) =
+                (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[8 * q + j]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)xreg[8 * q + 4 + j]) << 16);
         }
       }
     }
