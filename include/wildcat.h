@@ -44,7 +44,9 @@
  *  - Input values must be finite, and beta*<x,y>/tau^2 must stay inside the
  *    float32 exp range (|.| < 88) for key/key and query/key pairs; the
  *    library does not rescale.  Larger values give inf/NaN intermediates and
- *    clipped garbage outputs, not an error status.
+ *    clipped garbage outputs, not an error status, from the asynchronous
+ *    calls; wildcat_check_range checks this contract on the data (host-
+ *    synchronous) and returns WILDCAT_ERR_RANGE when it does not hold.
  */
 #ifndef WILDCAT_H
 #define WILDCAT_H
@@ -63,8 +65,14 @@ typedef enum {
   WILDCAT_ERR_DTYPE = -2,      /* dtype not one of wildcat_dtype */
   WILDCAT_ERR_SHAPE = -3,      /* sizes out of range (see the descriptors) */
   WILDCAT_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required */
-  WILDCAT_ERR_HIP = -6         /* a kernel launch failed */
+  WILDCAT_ERR_RANGE = -5,      /* wildcat_check_range: an exponent bound exceeds WILDCAT_RANGE_LIMIT */
+  WILDCAT_ERR_HIP = -6         /* a kernel launch or a copy failed */
 } wildcat_status;
+
+/* Largest exponent argument wildcat_check_range accepts.  exp(64) leaves a
+ * factor e^24 of float32 headroom for the sums over up to 2^21 keys and for
+ * |V| up to e^9. */
+#define WILDCAT_RANGE_LIMIT 64.0
 
 typedef enum { WILDCAT_FP32 = 0, WILDCAT_BF16 = 1 } wildcat_dtype;
 
@@ -162,6 +170,34 @@ wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q,
                               const void* K_S, const float* X,
                               const float* vmin, const float* vmax, float* O,
                               hipStream_t stream);
+
+/*
+ * Input-range guard  [WildCat: the exponential kernel h(q, k) = exp(beta
+ * <q, k>) of the problem statement, used here without a stabilising shift].
+ * Bounds every exponent argument the three calls can meet, by Cauchy-Schwarz:
+ *   E_k = beta / tau^2 * max_l |k_l|^2      (x4 with recentring:
+ *                                            |k - kbar| <= 2 max |k|)
+ *   E_q = beta * max_i |q_i| * max_l |k_l|  (only if qdesc and Q are given)
+ * over all units, with the squared norms summed in float64 on the GPU.
+ * HOST-SYNCHRONOUS: enqueues two small reductions on `stream`, copies two
+ * doubles back and synchronises `stream` before returning.  Not for capture
+ * into a graph.  Returns WILDCAT_ERR_RANGE if E_k or E_q exceeds
+ * WILDCAT_RANGE_LIMIT or is not finite (a NaN or inf input counts as inf).
+ *
+ *   desc, K     as for wildcat_select (K read only).
+ *   qdesc, Q    as for wildcat_attend, or both NULL; qdesc->d and
+ *               qdesc->dtype must equal desc->d and desc->dtype.
+ *   scratch     device, >= 2 doubles, 8-byte aligned; overwritten.
+ *   bounds      host, 2 doubles out (may be NULL): {E_k, E_q} (E_q = 0
+ *               without queries); written whenever the reductions ran.
+ * Argument problems return WILDCAT_ERR_ARG / _DTYPE / _SHAPE before any
+ * launch; WILDCAT_ERR_HIP if a launch, the copy or the synchronisation
+ * failed.
+ */
+wildcat_status wildcat_check_range(const wildcat_kv_desc* desc, const void* K,
+                                   const wildcat_q_desc* qdesc, const void* Q,
+                                   double* scratch, double* bounds,
+                                   hipStream_t stream);
 
 /* Host.  Static description of a status code. */
 const char* wildcat_status_string(wildcat_status status);

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwildcat.so")
-SOURCES = ["api.hip", "select.hip", "contract.hip", "trsm.hip"]
+SOURCES = ["api.hip", "select.hip", "contract.hip", "trsm.hip", "guard.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -14,12 +14,25 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
 hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
                          const void* K_S, const float* X, const float* vmin, const float* vmax, float* O,
                          hipStream_t st);
+hipError_t range_norms(int bf16, int d, const void* K, size_t krows, const void* Q, size_t qrows, double* scratch,
+                       double (&maxsq)[2], hipStream_t st);
 }  // namespace wc
 
 namespace {
 
 bool valid_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wildcat_status check_q(const wildcat_q_desc* q) {
+  if (q == nullptr) return WILDCAT_ERR_ARG;
+  if (q->dtype != WILDCAT_FP32 && q->dtype != WILDCAT_BF16) return WILDCAT_ERR_DTYPE;
+  if (!(isfinite(q->beta) && q->beta > 0.0)) return WILDCAT_ERR_ARG;
+  if (q->batch < 1 || q->kv_heads < 1 || q->q_heads < 1 || q->q_heads % q->kv_heads != 0 ||
+      q->m < 1 || q->m > (1 << 24) || !valid_d(q->d) || q->r < 1 || q->r > wc::kMaxR ||
+      (int64_t)q->batch * q->q_heads > 65535)
+    return WILDCAT_ERR_SHAPE;
+  return WILDCAT_OK;
+}
 
 wildcat_status check_kv(const wildcat_kv_desc* k) {
   if (k == nullptr) return WILDCAT_ERR_ARG;
@@ -79,19 +92,43 @@ wildcat_status wildcat_weights(const wildcat_kv_desc* desc, const void* K, const
 
 wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q, const void* K_S, const float* X,
                               const float* vmin, const float* vmax, float* O, hipStream_t stream) {
-  if (desc == nullptr) return WILDCAT_ERR_ARG;
-  if (desc->dtype != WILDCAT_FP32 && desc->dtype != WILDCAT_BF16) return WILDCAT_ERR_DTYPE;
-  if (!(isfinite(desc->beta) && desc->beta > 0.0)) return WILDCAT_ERR_ARG;
-  if (desc->batch < 1 || desc->kv_heads < 1 || desc->q_heads < 1 || desc->q_heads % desc->kv_heads != 0 ||
-      desc->m < 1 || desc->m > (1 << 24) || !valid_d(desc->d) || desc->r < 1 || desc->r > wc::kMaxR ||
-      (int64_t)desc->batch * desc->q_heads > 65535)
-    return WILDCAT_ERR_SHAPE;
+  const wildcat_status qs = check_q(desc);
+  if (qs != WILDCAT_OK) return qs;
   if (!Q || !K_S || !X || !vmin || !vmax || !O || !aligned16(Q) || !aligned16(K_S)) return WILDCAT_ERR_ARG;
   const int Uq = desc->batch * desc->q_heads;
   const int group = desc->q_heads / desc->kv_heads;
   hipError_t e = wc::launch_attend(desc->dtype == WILDCAT_BF16, Uq, group, desc->m, desc->d, desc->r, desc->beta,
                                    Q, K_S, X, vmin, vmax, O, stream);
   return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
+}
+
+wildcat_status wildcat_check_range(const wildcat_kv_desc* desc, const void* K, const wildcat_q_desc* qdesc,
+                                   const void* Q, double* scratch, double* bounds, hipStream_t stream) {
+  wildcat_status st = check_kv(desc);
+  if (st != WILDCAT_OK) return st;
+  if (!K || !aligned16(K) || !scratch || (reinterpret_cast<uintptr_t>(scratch) & 7u) != 0) return WILDCAT_ERR_ARG;
+  if ((qdesc == nullptr) != (Q == nullptr)) return WILDCAT_ERR_ARG;
+  size_t qrows = 0;
+  if (qdesc) {
+    if ((st = check_q(qdesc)) != WILDCAT_OK) return st;
+    if (!aligned16(Q)) return WILDCAT_ERR_ARG;
+    if (qdesc->dtype != desc->dtype) return WILDCAT_ERR_DTYPE;
+    if (qdesc->d != desc->d) return WILDCAT_ERR_SHAPE;
+    qrows = (size_t)qdesc->batch * qdesc->q_heads * qdesc->m;
+  }
+  const size_t krows = (size_t)desc->batch * desc->kv_heads * desc->n;
+  double maxsq[2];
+  const hipError_t e = wc::range_norms(desc->dtype == WILDCAT_BF16, desc->d, K, krows, Q, qrows, scratch, maxsq,
+                                       stream);
+  if (e != hipSuccess) return WILDCAT_ERR_HIP;
+  const double ek = desc->beta / (desc->tau * desc->tau) * maxsq[0] * (desc->recentre ? 4.0 : 1.0);
+  const double eq = qdesc ? qdesc->beta * sqrt(maxsq[1]) * sqrt(maxsq[0]) : 0.0;
+  if (bounds) {
+    bounds[0] = ek;
+    bounds[1] = eq;
+  }
+  if (!(ek <= WILDCAT_RANGE_LIMIT) || !(eq <= WILDCAT_RANGE_LIMIT)) return WILDCAT_ERR_RANGE;
+  return WILDCAT_OK;
 }
 
 const char* wildcat_status_string(wildcat_status status) {
@@ -101,6 +138,7 @@ const char* wildcat_status_string(wildcat_status status) {
     case WILDCAT_ERR_DTYPE: return "unsupported dtype";
     case WILDCAT_ERR_SHAPE: return "shape out of range";
     case WILDCAT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case WILDCAT_ERR_RANGE: return "an exponent bound of the inputs exceeds WILDCAT_RANGE_LIMIT (or is not finite)";
     case WILDCAT_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";

@@ -34,13 +34,15 @@ WILDCAT_ERR_ARG = -1
 WILDCAT_ERR_DTYPE = -2
 WILDCAT_ERR_SHAPE = -3
 WILDCAT_ERR_WORKSPACE = -4
+WILDCAT_ERR_RANGE = -5
 WILDCAT_ERR_HIP = -6
+RANGE_LIMIT = 64.0    # WILDCAT_RANGE_LIMIT
 WILDCAT_FP32 = 0
 WILDCAT_BF16 = 1
 
 EXPORTED = (
     "wildcat_select_workspace_bytes", "wildcat_weights_workspace_bytes", "wildcat_select",
-    "wildcat_weights", "wildcat_attend", "wildcat_status_string",
+    "wildcat_weights", "wildcat_attend", "wildcat_check_range", "wildcat_status_string",
 )
 
 
@@ -68,14 +70,17 @@ lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp,
 lib.wildcat_weights.restype = ctypes.c_int
 lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.wildcat_attend.restype = ctypes.c_int
+lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
+                                    ctypes.POINTER(ctypes.c_double), _vp]
+lib.wildcat_check_range.restype = ctypes.c_int
 lib.wildcat_status_string.argtypes = [ctypes.c_int]
 lib.wildcat_status_string.restype = ctypes.c_char_p
 
 
 class WildcatError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: str = ""):
         self.status = status
-        super().__init__(f"{where}: {lib.wildcat_status_string(status).decode()} (status {status})")
+        super().__init__(f"{where}: {lib.wildcat_status_string(status).decode()} (status {status}){detail}")
 
 
 def _check(status: int, where: str):
@@ -160,6 +165,25 @@ def attend(Q, K_S, X, vmin, vmax, beta, stream=None, out=None):
     _check(lib.wildcat_attend(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(O),
                               _stream(stream)), "wildcat_attend")
     return O
+
+
+def check_range(K, r, beta, tau=1.0, recentre=False, Q=None, scratch=None, stream=None):
+    """wildcat_check_range (host-synchronous): returns the exponent bounds
+    (E_k, E_q); raises WildcatError with status WILDCAT_ERR_RANGE when one
+    exceeds RANGE_LIMIT."""
+    desc = kv_desc(K, r, beta, tau, recentre)
+    qd = None
+    if Q is not None:
+        B, Hq, m, d = Q.shape
+        qd = QDesc(B, Hq, K.shape[1], m, d, int(r), float(beta), _dtype_code(Q))
+    buf = scratch if scratch is not None else torch.empty(2, dtype=torch.float64, device=K.device)
+    bounds = (ctypes.c_double * 2)()
+    st = lib.wildcat_check_range(ctypes.byref(desc), _ptr(K), ctypes.byref(qd) if qd is not None else None,
+                                 _ptr(Q), _ptr(buf), bounds, _stream(stream))
+    if st != WILDCAT_OK:
+        raise WildcatError(st, "wildcat_check_range",
+                           f": E_k = {bounds[0]:.4g}, E_q = {bounds[1]:.4g}" if st == WILDCAT_ERR_RANGE else "")
+    return bounds[0], bounds[1]
 
 
 def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None):

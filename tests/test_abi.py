@@ -101,6 +101,40 @@ def test_attend_rejects_bad_descriptors(kw, status):
     assert wc.lib.wildcat_attend(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
 
 
+def _q(**kw):
+    base = dict(batch=2, q_heads=8, kv_heads=4, m=64, d=128, r=256, beta=0.1, dtype=wc.WILDCAT_BF16)
+    base.update(kw)
+    return wc.QDesc(*[base[f] for f, _ in wc.QDesc._fields_])
+
+
+@pytest.mark.parametrize("kdesc,qdesc,status", [
+    (dict(d=100), None, wc.WILDCAT_ERR_SHAPE),
+    (dict(beta=-1.0), None, wc.WILDCAT_ERR_ARG),
+    (dict(), dict(d=64), wc.WILDCAT_ERR_SHAPE),          # query d differs from the keys'
+    (dict(), dict(dtype=wc.WILDCAT_FP32), wc.WILDCAT_ERR_DTYPE),
+    (dict(), dict(q_heads=6), wc.WILDCAT_ERR_SHAPE),     # not a multiple of kv_heads
+    (dict(), dict(m=0), wc.WILDCAT_ERR_SHAPE),
+])
+def test_check_range_rejects_bad_descriptors(kdesc, qdesc, status):
+    d = _kv(**kdesc)
+    q = _q(**qdesc) if qdesc is not None else None
+    got = wc.lib.wildcat_check_range(ctypes.byref(d), FAKE, ctypes.byref(q) if q is not None else None,
+                                     FAKE if q is not None else None, FAKE, None, None)
+    assert got == status
+
+
+def test_check_range_rejects_bad_pointers():
+    d, q = _kv(), _q()
+    cr = wc.lib.wildcat_check_range
+    assert cr(ctypes.byref(d), None, None, None, FAKE, None, None) == wc.WILDCAT_ERR_ARG
+    assert cr(ctypes.byref(d), FAKE, None, None, None, None, None) == wc.WILDCAT_ERR_ARG          # no scratch
+    assert cr(ctypes.byref(d), FAKE, None, None, ctypes.c_void_p((1 << 20) + 4), None, None) == wc.WILDCAT_ERR_ARG
+    assert cr(ctypes.byref(d), FAKE, ctypes.byref(q), None, FAKE, None, None) == wc.WILDCAT_ERR_ARG  # Q missing
+    assert cr(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, None) == wc.WILDCAT_ERR_ARG             # qdesc missing
+
+
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -6):
-        assert wc.lib.wildcat_status_string(s)
+    for st in (wc.WILDCAT_OK, wc.WILDCAT_ERR_ARG, wc.WILDCAT_ERR_DTYPE, wc.WILDCAT_ERR_SHAPE,
+               wc.WILDCAT_ERR_WORKSPACE, wc.WILDCAT_ERR_RANGE, wc.WILDCAT_ERR_HIP):
+        assert wc.lib.wildcat_status_string(st) and b"unknown" not in wc.lib.wildcat_status_string(st)
+    assert b"unknown" in wc.lib.wildcat_status_string(42)

@@ -184,3 +184,34 @@ def test_mixed_early_stop_across_unit_groups():
     assert [ref[h].sel.r_eff for h in range(H)] == [r, 3, r, 3, r]
     for h in range(H):
         _compare_unit(inp, g, h, ref[h])
+
+
+def test_check_range_bounds_and_error():
+    """wildcat_check_range: the exponent bounds it reports equal the
+    Cauchy-Schwarz bounds computed here from the same inputs; inputs scaled
+    past the limit, or holding a NaN, give WILDCAT_ERR_RANGE."""
+    import torch
+    from nystr_rpcholesky_coreset_amd import wildcat as wc
+    w = SMALL_CASES["kv_gqa8x2_ragged"]
+    inp = I.make_inputs(w)
+    K64 = I.to_f64(inp["K"], w.dtype)
+    Q64 = I.to_f64(inp["Q"], w.dtype)
+    mk = float((K64 ** 2).sum(-1).max())
+    mq = float((Q64 ** 2).sum(-1).max())
+    K = to_device(inp["K"], w.dtype)
+    Q = to_device(inp["Q"], w.dtype)
+    ek, eq = wc.check_range(K, w.r, w.beta, Q=Q)
+    assert abs(ek - w.beta * mk) <= 1e-12 * max(1.0, ek)
+    assert abs(eq - w.beta * np.sqrt(mq) * np.sqrt(mk)) <= 1e-12 * max(1.0, eq)
+    ek2, eq2 = wc.check_range(K, w.r, w.beta, tau=2.0, recentre=True)
+    assert abs(ek2 - w.beta * mk) <= 1e-12 * max(1.0, ek2) and eq2 == 0.0   # x4 / tau^2 = x1
+    big = (K.float() * 40.0).to(K.dtype)
+    with pytest.raises(wc.WildcatError) as e:
+        wc.check_range(big, w.r, w.beta)
+    assert e.value.status == wc.WILDCAT_ERR_RANGE
+    bad = K.clone()
+    bad.view(-1)[12345] = float("nan")
+    with pytest.raises(wc.WildcatError) as e:
+        wc.check_range(bad, w.r, w.beta)
+    assert e.value.status == wc.WILDCAT_ERR_RANGE
+    torch.cuda.synchronize()
