@@ -215,3 +215,38 @@ def test_check_range_bounds_and_error():
         wc.check_range(bad, w.r, w.beta)
     assert e.value.status == wc.WILDCAT_ERR_RANGE
     torch.cuda.synchronize()
+
+
+def test_concurrent_calls_on_two_streams_match_sequential():
+    """Two host threads run the whole path at once, each on its own
+    non-default stream (the library's auxiliary streams are shared between
+    them); every output must equal, bit for bit, the output of the same call
+    made alone on the default stream."""
+    import threading
+
+    import torch
+    cases = [SMALL_CASES["kv_gqa8x2_ragged"], SMALL_CASES["latent_h2"]]
+    inps = [I.make_inputs(w) for w in cases]
+    ref = [_run_gpu(inp) for inp in inps]
+    out = [None, None]
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    out[k] = _run_gpu(inps[k])
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(2):
+        for key in ("S", "r_eff", "L", "X", "O"):
+            np.testing.assert_array_equal(out[k][key], ref[k][key])
