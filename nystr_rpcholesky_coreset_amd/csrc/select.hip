@@ -414,6 +414,17 @@ __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(Sele
         ax3 = fma(f[q + 3].x, p3, ax3); ay3 = fma(f[q + 3].y, p3, ay3);
       }
     }
+    // Remainder: fours, then ones (short rounds spend a large share here).
+    for (; j + 4 <= je; j += 4) {
+      d2v f[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
+      Fp += 4 * ld;
+      ax0 = fma(f[0].x, s_prow[j], ax0); ay0 = fma(f[0].y, s_prow[j], ay0);
+      ax1 = fma(f[1].x, s_prow[j + 1], ax1); ay1 = fma(f[1].y, s_prow[j + 1], ay1);
+      ax2 = fma(f[2].x, s_prow[j + 2], ax2); ay2 = fma(f[2].y, s_prow[j + 2], ay2);
+      ax3 = fma(f[3].x, s_prow[j + 3], ax3); ay3 = fma(f[3].y, s_prow[j + 3], ay3);
+    }
     for (; j < je; ++j) {
       const d2v f0 = ld2<NT>(Fp);
       Fp += ld;
