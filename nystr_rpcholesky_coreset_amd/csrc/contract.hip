@@ -944,7 +944,7 @@ static hipError_t launch_prep_d(int d, int U, int n, int r, double c, int recent
 }
 
 hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
-                       const int32_t* r_eff, float* X, hipStream_t st);
+                       double* Dinv, const int32_t* r_eff, float* X, hipStream_t st);
 
 // CompressKV after selection: K_S, value range, Y = h_tau(K_S, K) [V, 1], X.
 hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
@@ -964,7 +964,8 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
   a.scale = (float)c;
   e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, lay.sp.nsplit, st);
   if (e != hipSuccess) return e;
-  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, reinterpret_cast<double*>(w + lay.LT), r_eff, X, st);
+  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, reinterpret_cast<double*>(w + lay.LT),
+                     reinterpret_cast<double*>(w + lay.Dinv), r_eff, X, st);
 }
 
 // WtdAttn: O = clip(h(Q, K_S) X / (h(Q, K_S) w)).

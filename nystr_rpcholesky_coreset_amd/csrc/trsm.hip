@@ -4,15 +4,19 @@
 // W = h_tau(K_S, K_S)^{-1} h_tau(K_S, K); with h_tau(K_S, K_S) = L L^T from the
 // Cholesky pivot block, W [V, 1] = L^{-T} L^{-1} (h_tau(K_S, K) [V, 1]).]
 //
-// One workgroup of NT threads (256 for r <= 256, else 1024) per (unit, group
-// of CPW right-hand-side columns), right-looking by tiles of 64 rows.  Thread
-// t owns rows t, t + NT, ... of the right-hand sides and keeps them in registers for the
-// whole solve, so the 64 rows of a tile belong to exactly one wave: that wave
-// solves the tile's 64x64 triangle (staged in LDS) with lane broadcasts and
-// publishes the solved values to LDS; then every thread subtracts the tile's
-// contribution from its own remaining rows, with independent coalesced loads
-// (L^T rows in the forward sweep, L rows in the backward sweep: consecutive
-// threads read consecutive doubles).  Y is summed from the split-n partials
+// Blocked by tiles of 64 rows with inverted diagonal blocks: one kernel
+// inverts every 64x64 diagonal block of L (one wave per block, column j of
+// the inverse by substitution in lane j, fp64); the solve then applies
+// L_tt^{-1} (forward) and L_tt^{-T} (backward) to a tile as a small
+// matrix-vector product, with no serial chain.  One workgroup of NT threads
+// (256 for r <= 256, else 1024) per (unit, group of CPW right-hand-side
+// columns), right-looking.  Thread t owns rows t, t + NT, ... of the
+// right-hand sides and keeps them in registers for the whole solve, so the
+// 64 rows of a tile belong to exactly one wave: that wave multiplies them by
+// the staged inverse block and publishes the solved values to LDS; then
+// every thread subtracts the tile's contribution from its own remaining rows,
+// with independent coalesced loads (L^T rows in the forward sweep, L rows in
+// the backward sweep: consecutive threads read consecutive doubles).  Y is summed from the split-n partials
 // of the contraction, in a fixed order, as the right-hand sides are loaded.
 // Only the first r_eff rows take part; rows past r_eff of X are written as 0.
 //
@@ -45,29 +49,78 @@ __global__ __launch_bounds__(kBlock) void transpose_l(const double* L, double* L
   }
 }
 
-// Broadcast lane k's double to the whole wave (k uniform).
-__device__ __forceinline__ double readlane_d(double v, int k) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), k);
-  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), k);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-// Diagonal 64x64 tile of L in LDS, XOR-swizzled so that both row-wise
-// (forward) and column-wise (backward) lane access are bank-conflict free.
+// A 64x64 block in LDS, XOR-swizzled so that both row-wise (forward) and
+// column-wise (backward) lane access are bank-conflict free.
 __device__ __forceinline__ int dt_idx(int a, int b) { return a * 64 + (b ^ a); }
 
-// Td <- L[i0 .. i0+nt)[i0 .. i0+nt) (zeros outside); each of the NT/64
-// waves takes 64 / (NT/64) rows.
+// Td <- a 64x64 block (row-major, leading dimension 64) of the inverses;
+// each of the NT/64 waves takes 64 / (NT/64) rows.
 template <int NT>
-__device__ __forceinline__ void stage_diag_wide(double* Td, const double* Lu, int r, int i0, int nt) {
+__device__ __forceinline__ void stage_inv_block(double* Td, const double* Dt) {
   constexpr int RW = 64 / (NT / 64);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < RW; ++q) {
     const int a = w * RW + q;
-    Td[dt_idx(a, lane)] = (a < nt && lane < nt) ? Lu[(size_t)(i0 + a) * r + i0 + lane] : 0.0;
+    Td[dt_idx(a, lane)] = Dt[a * 64 + lane];
   }
+}
+
+// One wave: zq <- B zq for the tile's rows (lane = row), B = the staged
+// inverse block (TRANS: its transpose).  The current values go to Zt first
+// (one wave's LDS accesses execute in order), then each lane forms its row
+// of the product; the solved values are left in Zt for the panel update.
+template <int CPW, bool TRANS>
+__device__ __forceinline__ void apply_inv_block(const double* Td, double* Zt, double (&zq)[CPW], int lane, int nt) {
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? zq[c] : 0.0;
+  double acc[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) acc[c] = 0.0;
+#pragma unroll 8
+  for (int k = 0; k < 64; ++k) {
+    const double b = TRANS ? Td[dt_idx(k, lane)] : Td[dt_idx(lane, k)];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) acc[c] = fma(b, Zt[k * CPW + c], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    zq[c] = lane < nt ? acc[c] : zq[c];
+    Zt[lane * CPW + c] = lane < nt ? acc[c] : 0.0;
+  }
+}
+
+// Dinv[u][tile] = inverse of the 64x64 diagonal block of L[u] at rows
+// 64 tile .. (only the first r_eff rows; the rest of the block is the
+// identity).  One wave per block: lane j computes column j of the inverse by
+// forward substitution, X[i][j] = (delta_ij - sum_{m<i} L[i][m] X[m][j]) /
+// L[i][i], with the block in LDS (row reads are broadcasts) and the columns
+// of X in LDS (lane j reads and writes its own column).
+__global__ __launch_bounds__(64) void invert_diag_blocks(const double* L, double* Dinv, const int32_t* r_eff,
+                                                         int r) {
+  __shared__ double Ls[64 * 65];
+  __shared__ double Xs[64 * 64];
+  const int tile = blockIdx.x, u = blockIdx.y, j = threadIdx.x;
+  const int i0 = tile * 64, re = r_eff[u];
+  const int nt = max(0, min(64, re - i0));
+  const double* Lu = L + (size_t)u * r * r;
+  for (int a = 0; a < 64; ++a)
+    Ls[a * 65 + j] = (a < nt && j < nt) ? Lu[(size_t)(i0 + a) * r + i0 + j] : (a == j ? 1.0 : 0.0);
+  __syncthreads();
+  for (int i = 0; i < 64; ++i) {
+    double a0 = i == j ? 1.0 : 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int m = 0;
+    for (; m + 4 <= i; m += 4) {
+      a0 = fma(-Ls[i * 65 + m], Xs[m * 64 + j], a0);
+      a1 = fma(-Ls[i * 65 + m + 1], Xs[(m + 1) * 64 + j], a1);
+      a2 = fma(-Ls[i * 65 + m + 2], Xs[(m + 2) * 64 + j], a2);
+      a3 = fma(-Ls[i * 65 + m + 3], Xs[(m + 3) * 64 + j], a3);
+    }
+    for (; m < i; ++m) a0 = fma(-Ls[i * 65 + m], Xs[m * 64 + j], a0);
+    Xs[i * 64 + j] = ((a0 + a1) + (a2 + a3)) / Ls[i * 65 + i];
+  }
+  double* Du = Dinv + ((size_t)u * (r / 64 + 1) + tile) * 64 * 64;
+  for (int i = 0; i < 64; ++i) Du[i * 64 + j] = Xs[i * 64 + j];
 }
 
 constexpr int kXcds = 8;
@@ -77,7 +130,8 @@ constexpr int kXcds = 8;
 
 template <int CPW, int RPT, int NT>
 __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, const double* L,
-                                                          const double* LT, const int32_t* r_eff, float* X, int r,
+                                                          const double* LT, const double* Dinv,
+                                                          const int32_t* r_eff, float* X, int r,
                                                           int D1, int U, int G) {
   __shared__ double Td[64 * 64];
   __shared__ double Zt[64 * CPW];
@@ -89,6 +143,7 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
   const int re = r_eff[u];
   const double* Lu = L + (size_t)u * r * r;
   const double* LTu = LT + (size_t)u * r * r;
+  const double* Du = Dinv + (size_t)u * (r / 64 + 1) * 64 * 64;
 
   // Right-hand sides: Y = sum over the contraction's splits, in split order.
   const size_t per_split = (size_t)U * r * D1;
@@ -122,31 +177,14 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
   for (int i0 = 0; i0 < re; i0 += 64) {
     const int nt = min(64, re - i0);
     const int qo = i0 / NT, wo = (i0 % NT) / 64;   // owner slot and wave
-    stage_diag_wide<NT>(Td, Lu, r, i0, nt);
+    stage_inv_block<NT>(Td, Du + (size_t)(i0 / 64) * 64 * 64);
     __syncthreads();
     if (wave == wo) {
       // The owner's rows (slot qo, a uniform branch per slot so that every
-      // index stays constant) are solved in registers with lane broadcasts;
-      // the updates are selects, not branches: the 64 steps are
-      // straight-line code.
+      // index stays constant): z_t <- L_tt^{-1} z_t, lane = row.
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q == qo) {
-          const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
-          for (int k = 0; k < nt; ++k) {
-            const double ik = readlane_d(inv, k);
-            const double lik = Td[dt_idx(lane, k)];
-            const bool below = lane > k && lane < nt, diag = lane == k;
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-              const double zk = readlane_d(z[q][c], k) * ik;
-              const double upd = fma(-lik, zk, z[q][c]);
-              z[q][c] = diag ? zk : (below ? upd : z[q][c]);
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
-        }
+        if (q == qo) apply_inv_block<CPW, false>(Td, Zt, z[q], lane, nt);
       }
     }
     __syncthreads();
@@ -174,27 +212,13 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
   for (int i0 = ((re - 1) / 64) * 64; re > 0 && i0 >= 0; i0 -= 64) {
     const int nt = min(64, re - i0);
     const int qo = i0 / NT, wo = (i0 % NT) / 64;
-    stage_diag_wide<NT>(Td, Lu, r, i0, nt);
+    stage_inv_block<NT>(Td, Du + (size_t)(i0 / 64) * 64 * 64);
     __syncthreads();
     if (wave == wo) {
+      // x_t <- L_tt^{-T} z_t.
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q == qo) {
-          const double inv = lane < nt ? 1.0 / Td[dt_idx(lane, lane)] : 0.0;
-          for (int k = nt - 1; k >= 0; --k) {
-            const double ik = readlane_d(inv, k);
-            const double lki = Td[dt_idx(k, lane)];
-            const bool above = lane < k, diag = lane == k;
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-              const double xk = readlane_d(z[q][c], k) * ik;
-              const double upd = fma(-lki, xk, z[q][c]);
-              z[q][c] = diag ? xk : (above ? upd : z[q][c]);
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? z[q][c] : 0.0;
-        }
+        if (q == qo) apply_inv_block<CPW, true>(Td, Zt, z[q], lane, nt);
       }
     }
     __syncthreads();
@@ -232,22 +256,23 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
 
 template <int CPW, int RPT, int NT>
 static void launch_trsm_t(int U, int r, int D1, const float* ypart, int nsplit, const double* L, const double* LT,
-                          const int32_t* r_eff, float* X, hipStream_t st) {
+                          const double* Dinv, const int32_t* r_eff, float* X, hipStream_t st) {
   const int G = (D1 + CPW - 1) / CPW;                      // column groups per unit
   const int slots = (U + kXcds - 1) / kXcds * G;          // workgroups per XCD
-  trsm_cols<CPW, RPT, NT><<<slots * kXcds, NT, 0, st>>>(ypart, nsplit, L, LT, r_eff, X, r, D1, U, G);
+  trsm_cols<CPW, RPT, NT><<<slots * kXcds, NT, 0, st>>>(ypart, nsplit, L, LT, Dinv, r_eff, X, r, D1, U, G);
 }
 
 // Threads and rows per thread: 256 x 1 up to r = 256, 1024 x 1 up to 1024,
 // 1024 x 2 up to 2048, 1024 x 4 up to 4096.
 hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
-                       const int32_t* r_eff, float* X, hipStream_t st) {
+                       double* Dinv, const int32_t* r_eff, float* X, hipStream_t st) {
   const int D1 = d + 1;
   transpose_l<<<dim3((r + 31) / 32, (r + 31) / 32, U), kBlock, 0, st>>>(L, LT, r);
-  if (r <= 256) launch_trsm_t<4, 1, 256>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
-  else if (r <= 1024) launch_trsm_t<4, 1, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
-  else if (r <= 2048) launch_trsm_t<4, 2, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
-  else launch_trsm_t<4, 4, 1024>(U, r, D1, ypart, nsplit, L, LT, r_eff, X, st);
+  invert_diag_blocks<<<dim3((r + 63) / 64, U), 64, 0, st>>>(L, Dinv, r_eff, r);
+  if (r <= 256) launch_trsm_t<4, 1, 256>(U, r, D1, ypart, nsplit, L, LT, Dinv, r_eff, X, st);
+  else if (r <= 1024) launch_trsm_t<4, 1, 1024>(U, r, D1, ypart, nsplit, L, LT, Dinv, r_eff, X, st);
+  else if (r <= 2048) launch_trsm_t<4, 2, 1024>(U, r, D1, ypart, nsplit, L, LT, Dinv, r_eff, X, st);
+  else launch_trsm_t<4, 4, 1024>(U, r, D1, ypart, nsplit, L, LT, Dinv, r_eff, X, st);
   return hipGetLastError();
 }
 

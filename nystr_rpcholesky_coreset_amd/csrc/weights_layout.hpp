@@ -44,11 +44,12 @@ struct ContractSplit {
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
 //   LT      [U][r][r]           fp64   transposed pivot block for the forward solve
+//   Dinv    [U][r/64+1][64][64] fp64   inverses of the 64x64 diagonal blocks of the pivot block
 constexpr int kMinMaxRows = 1024;   // rows of V per min/max partial
 struct WeightsLayout {
   ContractSplit sp;
   int nmm;
-  size_t ypart, mmpart, kbar, rowc, colc, LT, total;
+  size_t ypart, mmpart, kbar, rowc, colc, LT, Dinv, total;
   WeightsLayout(int U, int n, int d, int r, bool bf16) : sp(U, r, n, contract_rows_per_wg(d, r, bf16)) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
     size_t o = 0;
@@ -58,6 +59,7 @@ struct WeightsLayout {
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
     LT = o;     o += al256((size_t)U * r * r * 8);
+    Dinv = o;   o += al256((size_t)U * (r / 64 + 1) * 64 * 64 * 8);
     total = o;
   }
 };
