@@ -4,11 +4,13 @@ One step = wildcat_select + wildcat_weights + wildcat_attend over the whole
 synthetic workload (inputs already resident in HBM).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--bins B] [--no-cpu-baseline] [--copy-calibration]
 
 Default workload: KV-cache compression with GQA, 32 query heads over 8 kv
 heads, n = 32768 keys, d = 128, r = 1024 pivots per kv head, 64 queries per
-query head, bf16 inputs.
+query head, bf16 inputs.  --bins B > 1 times the binned variant (B contiguous
+key bins per kv head, r/B pivots and block-diagonal Nystroem weights per bin);
+the default B = 1 is plain RPNys.
 """
 from __future__ import annotations
 
@@ -29,17 +31,19 @@ MFMA_BF16_TFLOPS = 2500.0
 MFMA_FP32_TFLOPS = 157.3
 
 
-def select_bytes(w, e):
-    """Algorithmic HBM bytes of RPNys over all units: per unit and round i the
-    keys (n*d*e), the new factor column (8n), the residual diagonal read and
-    write (16n) and the previous factor columns (8*n*i)."""
-    U, n, d, r = w.units, w.n, w.d, w.r
+def select_bytes(w, e, bins=1):
+    """Algorithmic HBM bytes of RPNys over all units (and bins): per unit (bin)
+    and round i the keys (n*d*e), the new factor column (8n), the residual
+    diagonal read and write (16n) and the previous factor columns (8*n*i),
+    with n/B keys and r/B rounds per bin."""
+    U, n, d, r = w.units * bins, w.n // bins, w.d, w.r // bins
     return U * n * (r * (d * e + 24) + 4 * r * (r - 1))
 
 
-def contraction_flops(w):
-    """Matrix-core flops: scores and value products of both contractions."""
-    c1 = w.units * (2 * w.r * w.n * w.d + 2 * w.r * w.n * (w.d + 1))
+def contraction_flops(w, bins=1):
+    """Matrix-core flops: scores and value products of both contractions
+    (with bins, each bin's r/B pivots against its n/B keys)."""
+    c1 = w.units * bins * (2 * (w.r // bins) * (w.n // bins) * (2 * w.d + 1))
     c2 = w.q_units * (2 * w.m * w.r * w.d + 2 * w.m * w.r * (w.d + 1))
     return c1, c2
 
@@ -72,7 +76,7 @@ def measured_traffic(w):
         return None
 
 
-def cpu_baseline(w, inp, target_s=20.0):
+def cpu_baseline(w, inp, bins=1, target_s=20.0):
     """The oracle as it stands, timed on host cores on a bounded sample: whole
     kv units (select + weights + attend for their query heads), as many as fit
     in about target_s seconds (at least one)."""
@@ -91,7 +95,10 @@ def cpu_baseline(w, inp, target_s=20.0):
     units_done = 0
     for uidx in range(w.units):
         b, h = divmod(uidx, w.kv_heads)
-        ur = orc.compress_unit(K[b, h], V[b, h], inp["u"][uidx], w.r, w.beta, w.tau, w.recentre)
+        if bins == 1:
+            ur = orc.compress_unit(K[b, h], V[b, h], inp["u"][uidx], w.r, w.beta, w.tau, w.recentre)
+        else:
+            ur = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][uidx], w.r, bins, w.beta, w.tau, w.recentre)
         for hq in range(h * group, (h + 1) * group):
             Q = I.to_f64(Qa[b, hq], w.dtype)
             orc.plugin_attend(Q, ur.K_S, ur.X, ur.vmin, ur.vmax, w.beta)
@@ -112,6 +119,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--bins", type=int, default=1, help="key bins per kv head (1: plain RPNys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain elementwise kernel over 1 GiB (1 GiB read + 1 GiB write), "
@@ -141,7 +149,14 @@ def main():
 
     Q, K, V = to_dev(inp["Q"]), to_dev(inp["K"]), to_dev(inp["V"])
     u = torch.from_numpy(inp["u"]).to(dev)
-    desc = wc.kv_desc(K, w.r, w.beta, w.tau, w.recentre)
+    B = args.bins
+    if B < 1 or w.n % B or w.r % B:
+        print(f"--bins {B} must divide n = {w.n} and r = {w.r}", file=sys.stderr)
+        sys.exit(2)
+    rb = w.r // B
+    Kb, Vb = (wc.bin_view(K, B), wc.bin_view(V, B)) if B > 1 else (K, V)
+    ub = u.reshape(w.units * B, rb)
+    desc = wc.kv_desc(Kb, rb, w.beta, w.tau, w.recentre)
     ws_sel = torch.empty(wc.select_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     ws_w = torch.empty(wc.weights_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -149,10 +164,14 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        S, r_eff, L = wc.select(K, u, w.r, w.beta, w.tau, w.recentre, workspace=ws_sel)
+        S, r_eff, L = wc.select(Kb, ub, rb, w.beta, w.tau, w.recentre, workspace=ws_sel)
         if ev:
             ev[1].record(stream)
-        K_S, X, vmin, vmax = wc.weights(K, V, S, r_eff, L, w.r, w.beta, w.tau, w.recentre, workspace=ws_w)
+        K_S, X, vmin, vmax = wc.weights(Kb, Vb, S, r_eff, L, rb, w.beta, w.tau, w.recentre, workspace=ws_w)
+        if B > 1:
+            vmin, vmax = wc.merge_value_ranges(vmin, vmax, B)
+            K_S = K_S.view(w.batch, w.kv_heads, w.r, w.d)
+            X = X.view(w.batch, w.kv_heads, w.r, w.d + 1)
         if ev:
             ev[2].record(stream)
         O = wc.attend(Q, K_S, X, vmin, vmax, w.beta)
@@ -175,7 +194,7 @@ def main():
     t_sel, t_wts, t_att = (float(np.median(ph[:, j])) for j in range(3))
     ms_step = wall * 1000.0 / args.steps
     reff = r_eff.cpu().numpy()
-    assert np.all(reff == w.r), f"early stop on the bench workload: r_eff {reff}"
+    assert np.all(reff == rb), f"early stop on the bench workload: r_eff {reff}"
     assert torch.isfinite(O).all().item()
 
     if args.copy_calibration:
@@ -209,11 +228,11 @@ def main():
             continue
     del Ke, Ve
 
-    sb = select_bytes(w, e)
-    per_launch_bytes = sb / w.r
-    avg_launch_ms = t_sel / w.r
+    sb = select_bytes(w, e, B)
+    per_launch_bytes = sb / rb
+    avg_launch_ms = t_sel / rb
     achieved = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
-    c1, c2 = contraction_flops(w)
+    c1, c2 = contraction_flops(w, B)
     rows = w.query_rows
     value = rows / (ms_step * 1e-3)
     line = {
@@ -230,7 +249,7 @@ def main():
         "dtype": "f64+bf16" if w.dtype == "bf16" else "f64+fp32",
         "data": f"synthetic (seeded '{w.recipe}' recipe with the shapes of the {w.name} workload)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-                   "n": w.n, "m": w.m, "d": w.d, "r": w.r, "beta": w.beta, "input_dtype": w.dtype},
+                   "n": w.n, "m": w.m, "d": w.d, "r": w.r, "bins": B, "beta": w.beta, "input_dtype": w.dtype},
         "phases_ms": {"select": t_sel, "weights": t_wts, "attend": t_att},
         "rpcholesky_ms": t_sel,
         "select_hbm_frac": sb / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -238,21 +257,22 @@ def main():
         "attend_only_rows_per_s": rows / (t_att * 1e-3),
         "exact_attention_gpu": exact,
         "roofline": {
-            "kernel": "one RPNys round over all units: rpc_step (factor/diagonal stream) + rpc_draw (next pivot) "
+            "kernel": "one RPNys round over all units" + (f" and their {B} bins" if B > 1 else "")
+                      + ": rpc_step (factor/diagonal stream) + rpc_draw (next pivot) "
                       "of every unit group, the groups overlapped on their own streams",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(w),
+            "traffic": measured_traffic(w) if B == 1 else None,
             "traffic_unit": "bytes per round (rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000)",
             "bytes_per_launch": per_launch_bytes,
             "avg_launch_ms": avg_launch_ms,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
+        line["cpu_baseline"] = cpu_baseline(w, inp, B)
     print(json.dumps(line), flush=True)
 
 

@@ -172,6 +172,32 @@ wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q,
                               hipStream_t stream);
 
 /*
+ * Binned RPNys  [WildCat, RPNys / Alg. 1 paragraph: the divide-and-conquer
+ * strategy with B bins and a coreset of size r/B per bin, O(nr^2/B^2 + nrd/B)
+ * operations].  The bins of a unit are B contiguous blocks of n/B keys, each
+ * an independent RPNys problem with its own Nystroem weights (block-diagonal
+ * W), and the coreset is the bins' coresets in bin order.  Because the bins
+ * are contiguous, the bin-major view of the inputs is the same memory:
+ *   K, V   [batch][kv_heads * B][n/B][d]     u  [U * B][r/B]
+ * so wildcat_select and wildcat_weights run binning unchanged on a descriptor
+ * with kv_heads * B heads, n/B keys and rank r/B (S then holds indices local
+ * to each bin, r_eff is per bin).  Their outputs K_S [batch][kv_heads*B][r/B][d]
+ * and X [..][r/B][d+1] are, as memory, the concatenated per-unit coresets
+ * [batch][kv_heads][r][d] and [..][r][d+1] that wildcat_attend takes with
+ * rank r.  The one step in between is this call: the value range that attend
+ * clips to is over all n rows of the unit, i.e. the min / max over its bins.
+ *
+ *   units       batch * kv_heads;  bins >= 1, units * bins <= 65535;
+ *               d in {16, 32, 64, 128}.
+ *   vmin_bins, vmax_bins  [units * bins][d] float32 (wildcat_weights on the
+ *               bin-major view), read only.
+ *   vmin, vmax  [units][d] float32 out.
+ */
+wildcat_status wildcat_merge_value_ranges(int32_t units, int32_t bins, int32_t d,
+                                          const float* vmin_bins, const float* vmax_bins,
+                                          float* vmin, float* vmax, hipStream_t stream);
+
+/*
  * Input-range guard  [WildCat: the exponential kernel h(q, k) = exp(beta
  * <q, k>) of the problem statement, used here without a stabilising shift].
  * Bounds every exponent argument the three calls can meet, by Cauchy-Schwarz:

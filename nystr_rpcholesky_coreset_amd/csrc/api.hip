@@ -16,6 +16,8 @@ hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, doubl
                          hipStream_t st);
 hipError_t range_norms(int bf16, int d, const void* K, size_t krows, const void* Q, size_t qrows, double* scratch,
                        double (&maxsq)[2], hipStream_t st);
+hipError_t launch_merge_ranges(int units, int bins, int d, const float* vmin_b, const float* vmax_b, float* vmin,
+                               float* vmax, hipStream_t st);
 }  // namespace wc
 
 namespace {
@@ -129,6 +131,14 @@ wildcat_status wildcat_check_range(const wildcat_kv_desc* desc, const void* K, c
   }
   if (!(ek <= WILDCAT_RANGE_LIMIT) || !(eq <= WILDCAT_RANGE_LIMIT)) return WILDCAT_ERR_RANGE;
   return WILDCAT_OK;
+}
+
+wildcat_status wildcat_merge_value_ranges(int32_t units, int32_t bins, int32_t d, const float* vmin_bins,
+                                          const float* vmax_bins, float* vmin, float* vmax, hipStream_t stream) {
+  if (units < 1 || bins < 1 || !valid_d(d) || (int64_t)units * bins > 65535) return WILDCAT_ERR_SHAPE;
+  if (!vmin_bins || !vmax_bins || !vmin || !vmax) return WILDCAT_ERR_ARG;
+  const hipError_t e = wc::launch_merge_ranges(units, bins, d, vmin_bins, vmax_bins, vmin, vmax, stream);
+  return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
 }
 
 const char* wildcat_status_string(wildcat_status status) {

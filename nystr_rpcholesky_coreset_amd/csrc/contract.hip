@@ -843,6 +843,29 @@ __global__ __launch_bounds__(kBlock) void value_range_final(const float* part, f
   vmax[e] = mx;
 }
 
+// Binned RPNys: the value range of a unit is the min / max over its bins'
+// ranges (bins in order; min and max are exact, so the order is immaterial).
+__global__ __launch_bounds__(kBlock) void merge_ranges(const float* vmin_b, const float* vmax_b, float* vmin,
+                                                       float* vmax, int units, int bins, int d) {
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= units * d) return;
+  const int u = e / d, c = e % d;
+  float mn = vmin_b[((size_t)u * bins) * d + c], mx = vmax_b[((size_t)u * bins) * d + c];
+  for (int b = 1; b < bins; ++b) {
+    mn = fminf(mn, vmin_b[((size_t)u * bins + b) * d + c]);
+    mx = fmaxf(mx, vmax_b[((size_t)u * bins + b) * d + c]);
+  }
+  vmin[e] = mn;
+  vmax[e] = mx;
+}
+
+hipError_t launch_merge_ranges(int units, int bins, int d, const float* vmin_b, const float* vmax_b, float* vmin,
+                               float* vmax, hipStream_t st) {
+  merge_ranges<<<(unsigned)((units * d + kBlock - 1) / kBlock), kBlock, 0, st>>>(vmin_b, vmax_b, vmin, vmax, units,
+                                                                                   bins, d);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- host side
 // Key split of the bf16 attend contraction (d >= 32): when the query row
 // tiles alone give fewer than 256 workgroups (few query rows per head), a

@@ -42,7 +42,8 @@ WILDCAT_BF16 = 1
 
 EXPORTED = (
     "wildcat_select_workspace_bytes", "wildcat_weights_workspace_bytes", "wildcat_select",
-    "wildcat_weights", "wildcat_attend", "wildcat_check_range", "wildcat_status_string",
+    "wildcat_weights", "wildcat_attend", "wildcat_merge_value_ranges", "wildcat_check_range",
+    "wildcat_status_string",
 )
 
 
@@ -70,6 +71,8 @@ lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp,
 lib.wildcat_weights.restype = ctypes.c_int
 lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.wildcat_attend.restype = ctypes.c_int
+lib.wildcat_merge_value_ranges.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+lib.wildcat_merge_value_ranges.restype = ctypes.c_int
 lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
                                     ctypes.POINTER(ctypes.c_double), _vp]
 lib.wildcat_check_range.restype = ctypes.c_int
@@ -184,6 +187,45 @@ def check_range(K, r, beta, tau=1.0, recentre=False, Q=None, scratch=None, strea
         raise WildcatError(st, "wildcat_check_range",
                            f": E_k = {bounds[0]:.4g}, E_q = {bounds[1]:.4g}" if st == WILDCAT_ERR_RANGE else "")
     return bounds[0], bounds[1]
+
+
+def merge_value_ranges(vmin_bins, vmax_bins, bins, stream=None):
+    """wildcat_merge_value_ranges: [B][H*bins][d] per-bin ranges -> [B][H][d]."""
+    Bt, HB, d = vmin_bins.shape
+    H = HB // bins
+    vmin = torch.empty((Bt, H, d), dtype=torch.float32, device=vmin_bins.device)
+    vmax = torch.empty_like(vmin)
+    _check(lib.wildcat_merge_value_ranges(Bt * H, bins, d, _ptr(vmin_bins), _ptr(vmax_bins), _ptr(vmin), _ptr(vmax),
+                                          _stream(stream)), "wildcat_merge_value_ranges")
+    return vmin, vmax
+
+
+def bin_view(T, bins):
+    """[B][H][n][d] -> the bin-major view [B][H*bins][n/bins][d] (same memory)."""
+    Bt, H, n, d = T.shape
+    if n % bins:
+        raise ValueError(f"n = {n} is not a multiple of bins = {bins}")
+    return T.view(Bt, H * bins, n // bins, d)
+
+
+def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=None):
+    """Binned WildCat: select and weights on the bin-major view (each bin an
+    RPNys problem with r/bins pivots), per-unit value ranges, attend over the
+    concatenated coreset.  Returns (O, parts); parts["S"] holds indices local
+    to each bin, [B*H*bins][r/bins]."""
+    if r % bins:
+        raise ValueError(f"r = {r} is not a multiple of bins = {bins}")
+    Bt, H, n, d = K.shape
+    rb = r // bins
+    Kb, Vb = bin_view(K, bins), bin_view(V, bins)
+    ub = u.reshape(Bt * H * bins, rb)
+    S, r_eff, L = select(Kb, ub, rb, beta, tau, recentre, stream=stream)
+    K_S, X, vmin_b, vmax_b = weights(Kb, Vb, S, r_eff, L, rb, beta, tau, recentre, stream=stream)
+    vmin, vmax = merge_value_ranges(vmin_b, vmax_b, bins, stream=stream)
+    K_S = K_S.view(Bt, H, r, d)
+    X = X.view(Bt, H, r, d + 1)
+    O = attend(Q, K_S, X, vmin, vmax, beta, stream=stream)
+    return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)
 
 
 def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None):

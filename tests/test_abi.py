@@ -138,3 +138,13 @@ def test_status_strings():
                wc.WILDCAT_ERR_WORKSPACE, wc.WILDCAT_ERR_RANGE, wc.WILDCAT_ERR_HIP):
         assert wc.lib.wildcat_status_string(st) and b"unknown" not in wc.lib.wildcat_status_string(st)
     assert b"unknown" in wc.lib.wildcat_status_string(42)
+
+
+def test_merge_value_ranges_validation():
+    mv = wc.lib.wildcat_merge_value_ranges
+    assert mv(0, 4, 128, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
+    assert mv(8, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
+    assert mv(8, 4, 100, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
+    assert mv(40000, 2, 64, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
+    assert mv(8, 4, 128, None, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_ARG
+    assert mv(8, 4, 128, FAKE, FAKE, FAKE, None, None) == wc.WILDCAT_ERR_ARG
