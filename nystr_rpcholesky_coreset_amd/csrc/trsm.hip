@@ -94,33 +94,36 @@ __device__ __forceinline__ void apply_inv_block(const double* Td, double* Zt, do
 // 64 tile .. (only the first r_eff rows; the rest of the block is the
 // identity).  One wave per block: lane j computes column j of the inverse by
 // forward substitution, X[i][j] = (delta_ij - sum_{m<i} L[i][m] X[m][j]) /
-// L[i][i], with the block in LDS (row reads are broadcasts) and the columns
-// of X in LDS (lane j reads and writes its own column).
+// L[i][i], with the block in LDS (row reads are broadcasts) and column j in
+// the lane's registers (the loops are unrolled, so every index is constant).
 __global__ __launch_bounds__(64) void invert_diag_blocks(const double* L, double* Dinv, const int32_t* r_eff,
                                                          int r) {
-  __shared__ double Ls[64 * 65];
-  __shared__ double Xs[64 * 64];
+  __shared__ double Ls[64 * 64];
   const int tile = blockIdx.x, u = blockIdx.y, j = threadIdx.x;
   const int i0 = tile * 64, re = r_eff[u];
   const int nt = max(0, min(64, re - i0));
   const double* Lu = L + (size_t)u * r * r;
   for (int a = 0; a < 64; ++a)
-    Ls[a * 65 + j] = (a < nt && j < nt) ? Lu[(size_t)(i0 + a) * r + i0 + j] : (a == j ? 1.0 : 0.0);
+    Ls[a * 64 + j] = (a < nt && j < nt) ? Lu[(size_t)(i0 + a) * r + i0 + j] : (a == j ? 1.0 : 0.0);
   __syncthreads();
+  double x[64];
+#pragma unroll
   for (int i = 0; i < 64; ++i) {
     double a0 = i == j ? 1.0 : 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int m = 0;
-    for (; m + 4 <= i; m += 4) {
-      a0 = fma(-Ls[i * 65 + m], Xs[m * 64 + j], a0);
-      a1 = fma(-Ls[i * 65 + m + 1], Xs[(m + 1) * 64 + j], a1);
-      a2 = fma(-Ls[i * 65 + m + 2], Xs[(m + 2) * 64 + j], a2);
-      a3 = fma(-Ls[i * 65 + m + 3], Xs[(m + 3) * 64 + j], a3);
+#pragma unroll
+    for (int m = 0; m + 4 <= i; m += 4) {
+      a0 = fma(-Ls[i * 64 + m], x[m], a0);
+      a1 = fma(-Ls[i * 64 + m + 1], x[m + 1], a1);
+      a2 = fma(-Ls[i * 64 + m + 2], x[m + 2], a2);
+      a3 = fma(-Ls[i * 64 + m + 3], x[m + 3], a3);
     }
-    for (; m < i; ++m) a0 = fma(-Ls[i * 65 + m], Xs[m * 64 + j], a0);
-    Xs[i * 64 + j] = ((a0 + a1) + (a2 + a3)) / Ls[i * 65 + i];
+#pragma unroll
+    for (int m = i & ~3; m < i; ++m) a0 = fma(-Ls[i * 64 + m], x[m], a0);
+    x[i] = ((a0 + a1) + (a2 + a3)) / Ls[i * 64 + i];
   }
   double* Du = Dinv + ((size_t)u * (r / 64 + 1) + tile) * 64 * 64;
-  for (int i = 0; i < 64; ++i) Du[i * 64 + j] = Xs[i * 64 + j];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) Du[i * 64 + j] = x[i];
 }
 
 constexpr int kXcds = 8;
