@@ -7,7 +7,8 @@
 // at the pivot and downdates the residual diagonal.  Only the factor columns,
 // the diagonal and n kernel entries per round are touched (O(nr) entries).
 //
-// GPU structure (one launch per round, all units in one grid):
+// GPU structure (units in groups, one streaming launch per round and group,
+// see launch_select_t):
 //   * workgroup (blk, u) owns 128 consecutive keys of unit u, two per lane;
 //     its 4 waves split the previous factor columns j < i (and the key
 //     dimensions) into quarters, so every wave streams its own contiguous run
@@ -20,12 +21,14 @@
 //   * wave 0 finishes the rows: kernel value, new factor column, residual
 //     downdate, and a wave-level inclusive prefix sum of the new residuals
 //     whose total goes to a per-workgroup slot;
-//   * a separate one-workgroup-per-unit launch then draws the next pivot with
-//     a two-level inverse CDF over those totals and gathers F[s, :i+1] and
-//     k_s for the next round.  Splitting the draw off keeps the streaming
-//     kernel free of device-scope fences and atomics (on gfx950 every
-//     device-scope release fence writes back the XCD's L2); the kernel
-//     boundary publishes the round's results once.
+//   * one workgroup per unit, in a later launch, then draws the next pivot
+//     with a two-level inverse CDF over those totals and gathers F[s, :i+1]
+//     and k_s for the next round (rpc_draw, or extra workgroups of the other
+//     group's streaming launch in rpc_fused).  Keeping the draw out of the
+//     launch that produced its inputs keeps the streaming kernel free of
+//     device-scope fences and atomics (on gfx950 every device-scope release
+//     fence writes back the XCD's L2); the kernel boundary publishes the
+//     round's results once.
 // The draw is in fp64 with a fixed summation order: the prefix C_l of an index
 // is (exclusive prefix of its workgroup total) + (in-workgroup inclusive
 // prefix), T is C of the last index, and the pivot is the first l with
