@@ -150,12 +150,38 @@ def _rows_sphere(rng, rows, d, radius):
     return radius * z / np.sqrt((z * z).sum(axis=1, keepdims=True))
 
 
-def _gen(w: Workload, rng):
+def _new_rows(w: Workload, rng, mu, rows, d):
+    """Keys and values of `rows` tokens that follow the cached sequence: the
+    recipe's per-row law, with the unit's own mixture means; the sink scaling
+    of the first positions does not apply (those positions are in the cache)."""
+    sd = 1.0 / math.sqrt(d)
+    if w.recipe == "unit_ball":
+        return _rows_unit_ball(rng, rows, d), _rows_unit_ball(rng, rows, d)
+    if w.recipe == "vit_outliers":
+        k = sd * rng.standard_normal((rows, d))
+        v = sd * rng.standard_normal((rows, d))
+        idx = rng.choice(rows, size=int(math.floor(0.05 * rows)), replace=False)
+        k[idx] *= 3.0
+        return k, v
+    if w.recipe == "mixture16":
+        lab = rng.integers(0, 16, size=rows)
+        return mu[lab] + 0.3 * rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    if w.recipe == "kv_sinks":
+        return sd * rng.standard_normal((rows, d)), sd * rng.standard_normal((rows, d))
+    if w.recipe == "sphere2":
+        return _rows_sphere(rng, rows, d, 2.0), rng.standard_normal((rows, d))
+    raise ValueError(w.recipe)
+
+
+def _gen(w: Workload, rng, rng_new=None):
     B, Hq, Hkv, m, n, d = w.batch, w.q_heads, w.kv_heads, w.m, w.n, w.d
     group = Hq // Hkv
     Q = np.empty((B, Hq, m, d), dtype=w.storage_dtype)
     K = np.empty((B, Hkv, n, d), dtype=w.storage_dtype)
     V = np.empty((B, Hkv, n, d), dtype=w.storage_dtype)
+    if rng_new is not None:
+        K_new = np.empty((B, Hkv, m, d), dtype=w.storage_dtype)
+        V_new = np.empty((B, Hkv, m, d), dtype=w.storage_dtype)
     sd = 1.0 / math.sqrt(d)
     means = {}
     for b in range(B):
@@ -186,6 +212,10 @@ def _gen(w: Workload, rng):
                 raise ValueError(w.recipe)
             K[b, h] = _store(k, w.dtype)
             V[b, h] = _store(v, w.dtype)
+            if rng_new is not None:
+                kn, vn = _new_rows(w, rng_new, means.get((b, h)), m, d)
+                K_new[b, h] = _store(kn, w.dtype)
+                V_new[b, h] = _store(vn, w.dtype)
     for b in range(B):
         for h in range(Hq):
             if w.recipe == "unit_ball":
@@ -201,6 +231,8 @@ def _gen(w: Workload, rng):
             else:
                 raise ValueError(w.recipe)
             Q[b, h] = _store(q, w.dtype)
+    if rng_new is not None:
+        return Q, K, V, K_new, V_new
     return Q, K, V
 
 
@@ -209,10 +241,20 @@ def make_uniforms(w: Workload) -> np.ndarray:
     return np.random.default_rng(w.seed + 1000).random((w.units, w.r))
 
 
-def make_inputs(w: Workload) -> dict:
-    """Q, K, V (fp32 values or bf16 bit patterns as uint16) and uniforms u."""
+def make_inputs(w: Workload, new_tokens: bool = False) -> dict:
+    """Q, K, V (fp32 values or bf16 bit patterns as uint16) and uniforms u.
+
+    With new_tokens, also K_new, V_new [batch][kv_heads][m][d]: the keys and
+    values of m tokens that follow the n cached ones, drawn from their own
+    seed (seed + 2000, so Q, K, V and u are the same either way); query row i
+    of every query head is then the query of new token i.
+    """
     if w.q_heads % w.kv_heads:
         raise ValueError("q_heads must be a multiple of kv_heads")
     rng = np.random.default_rng(w.seed)
-    Q, K, V = _gen(w, rng)
-    return {"Q": Q, "K": K, "V": V, "u": make_uniforms(w), "workload": w}
+    out = {"u": make_uniforms(w), "workload": w}
+    if new_tokens:
+        out["Q"], out["K"], out["V"], out["K_new"], out["V_new"] = _gen(w, rng, np.random.default_rng(w.seed + 2000))
+    else:
+        out["Q"], out["K"], out["V"] = _gen(w, rng)
+    return out

@@ -272,6 +272,62 @@ def exact_attention(Q, K, V, beta):
 
 
 # --------------------------------------------------------------------------
+# Generation over a compressed cache
+# --------------------------------------------------------------------------
+def decode_attend(Q, K_S, X, vmin, vmax, K_new, V_new, beta):
+    """Generation over a compressed cache: m new tokens, causal among themselves.
+
+    [WildCat, KV-cache paragraph: after CompressKV the compressed keys and
+    values enter later attention computations (the decoding phase) through
+    WtdAttn, and m new tokens cost O(rmd + m^2 d) instead of the full prefix;
+    WtdAttn / Alg. 3; Lem. 1 paragraph (clip to the value range).]
+    Readings (the pages give no formula for this step):
+      * new token j joins the weighted attention as one more coreset point
+        with weight 1 and value v_j (its row of W is a unit vector: it is kept
+        exactly), so N_i = h(q_i, K_S) X + sum_{j <= i} h(q_i, k_j) [v_j, 1];
+      * causal: query i (the query of new token i) sees the whole compressed
+        prefix and the new tokens 0 .. i;
+      * the clip range of query i is the prefix range widened by v_0 .. v_i
+        (the values of every key it sees), taken with fmin / fmax so that a
+        NaN value leaves the range as it was.
+    Q, K_new, V_new: m x d (row i is new token i); K_S: r x d raw coreset keys
+    (r may be 0); X: r x (d+1); vmin, vmax: the prefix's column range.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K_new = np.asarray(K_new, dtype=np.float64)
+    V_new = np.asarray(V_new, dtype=np.float64)
+    m, d = Q.shape
+    N = query_kernel(Q, np.asarray(K_S, dtype=np.float64).reshape(-1, d), beta) @ np.asarray(X, dtype=np.float64).reshape(-1, d + 1)
+    A = np.tril(query_kernel(Q, K_new, beta))
+    N = N + A @ np.hstack([V_new, np.ones((m, 1))])
+    lo = np.fmin(np.asarray(vmin, dtype=np.float64)[None, :], np.fmin.accumulate(V_new, axis=0))
+    hi = np.fmax(np.asarray(vmax, dtype=np.float64)[None, :], np.fmax.accumulate(V_new, axis=0))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = N[:, :d] / N[:, d:d + 1]
+    return np.fmin(np.fmax(ratio, lo), hi)
+
+
+def wildcat_decode(Q, K_S, X, vmin, vmax, K_new, V_new, beta):
+    """decode_attend over all heads: Q [B][Hq][m][d]; K_S [B][Hkv][r][d];
+    X [B][Hkv][r][d+1]; vmin, vmax [B][Hkv][d]; K_new, V_new [B][Hkv][m][d].
+
+    Query head h reads kv head h // (Hq / Hkv), as in wildcat_forward.
+    Returns O [B][Hq][m][d].
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    B, Hq, m, d = Q.shape
+    Hkv = K_new.shape[1]
+    group = Hq // Hkv
+    O = np.empty((B, Hq, m, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            O[b, h] = decode_attend(Q[b, h], K_S[b, g], X[b, g], vmin[b, g], vmax[b, g], K_new[b, g], V_new[b, g],
+                                    beta)
+    return O
+
+
+# --------------------------------------------------------------------------
 # The whole path for one unit and for a batch of units
 # --------------------------------------------------------------------------
 @dataclass

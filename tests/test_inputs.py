@@ -45,3 +45,20 @@ def test_recipes_statistics():
     x = I.make_inputs(w)
     nr = np.linalg.norm(I.to_f64(x["K"], "bf16"), axis=-1)
     assert np.allclose(nr, 2.0, atol=0.02)
+
+
+def test_new_tokens_leave_the_cached_inputs_unchanged():
+    for name in I.WORKLOAD_ORDER:
+        w = I.scaled_workload(I.WORKLOADS[name], batch=1, q_heads=2, kv_heads=1, n=200, m=40, r=8)
+        a, b = I.make_inputs(w), I.make_inputs(w, new_tokens=True)
+        for k in "QKVu":
+            np.testing.assert_array_equal(a[k], b[k])
+        assert b["K_new"].shape == b["V_new"].shape == (1, 1, 40, w.d)
+        assert b["K_new"].dtype == w.storage_dtype
+        kn = I.to_f64(b["K_new"], w.dtype)
+        assert np.all(np.isfinite(kn)) and not np.array_equal(kn, I.to_f64(a["K"], w.dtype)[:, :, :40])
+    # the sink scaling belongs to the first cached positions only
+    w = I.scaled_workload(I.WORKLOADS["kvcache_gqa32x8_n32768_d128_r1024_bf16"], q_heads=1, kv_heads=1, n=64, m=64, r=8)
+    b = I.make_inputs(w, new_tokens=True)
+    norms = np.linalg.norm(I.to_f64(b["K_new"], w.dtype)[0, 0], axis=1)
+    assert norms.max() < 3.0
