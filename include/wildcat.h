@@ -14,6 +14,8 @@
  *   wildcat_attend  -- WtdAttn (Alg. 3): O_hat = diag(U w)^{-1} U V_S with
  *                      U = h(Q, K_S), each entry clipped to [v_min j, v_max j].
  * Calling the three in order on one stream is the WildCat module (Alg. 4).
+ *   wildcat_decode  -- generation over the cache: m new tokens attend to the
+ *                      coreset and, causally, to each other.
  *
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers unless a comment says "host".
@@ -169,6 +171,41 @@ wildcat_status wildcat_weights(const wildcat_kv_desc* desc, const void* K,
 wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q,
                               const void* K_S, const float* X,
                               const float* vmin, const float* vmax, float* O,
+                              hipStream_t stream);
+
+/*
+ * Generation over the compressed cache  [WildCat, KV-cache paragraph: the
+ * compressed keys and values enter the decoding phase through WtdAttn, and
+ * m new tokens cost O(rmd + m^2 d); WtdAttn / Alg. 3; Lem. 1 paragraph].
+ * The pages give no formula for this step; the reading taken: new token j
+ * joins the weighted attention as one more point of weight 1 and value v_j,
+ * seen by the queries of tokens i >= j (causal), and the clip range of query
+ * i is the cache's range widened by v_0 .. v_i.  Per query row i of query
+ * head h (kv unit as above):
+ *   N_i = sum_{l<r} exp(beta <q_i, K_S[l]>) X[l, :]
+ *       + sum_{j<=i} exp(beta <q_i, K_new[j]>) [V_new[j], 1]       (d+1 numbers)
+ *   lo_i[c] = fmin(vmin[c], V_new[0][c], .., V_new[i][c]), hi_i likewise (fmax)
+ *   O[i][c] = fmin(fmax(N_i[c] / N_i[d], lo_i[c]), hi_i[c])
+ * desc->m is the number of new tokens and query rows per head; desc->r the
+ * rank of the cache.  The kernel exponents are not shifted: the exponent
+ * contract of wildcat_check_range covers K_new like the cached keys.
+ *
+ *   Q           [batch][q_heads][m][d] dtype, read only: query row i is the
+ *               query of new token i.
+ *   K_S, X, vmin, vmax: the cache, as for wildcat_attend (r rows per unit).
+ *   K_new, V_new [batch][kv_heads][m][d] dtype, read only: the new tokens'
+ *               keys and values, in token order.
+ *   O           [batch][q_heads][m][d] float32 out.
+ *   workspace   >= wildcat_decode_workspace_bytes(desc) bytes, 16-byte
+ *               aligned; contents on entry do not matter.  Holds the staged
+ *               cache-plus-tokens operand and the running ranges.
+ */
+size_t wildcat_decode_workspace_bytes(const wildcat_q_desc* desc);
+wildcat_status wildcat_decode(const wildcat_q_desc* desc, const void* Q,
+                              const void* K_S, const float* X,
+                              const float* vmin, const float* vmax,
+                              const void* K_new, const void* V_new, float* O,
+                              void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
 /*

@@ -14,6 +14,9 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
 hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
                          const void* K_S, const float* X, const float* vmin, const float* vmax, float* O,
                          hipStream_t st);
+hipError_t launch_decode(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
+                         const void* K_S, const float* X, const float* vmin, const float* vmax, const void* Kn,
+                         const void* Vn, float* O, void* ws, hipStream_t st);
 hipError_t range_norms(int bf16, int d, const void* K, size_t krows, const void* Q, size_t qrows, double* scratch,
                        double (&maxsq)[2], hipStream_t st);
 hipError_t launch_merge_ranges(int units, int bins, int d, const float* vmin_b, const float* vmax_b, float* vmin,
@@ -101,6 +104,27 @@ wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q, const v
   const int group = desc->q_heads / desc->kv_heads;
   hipError_t e = wc::launch_attend(desc->dtype == WILDCAT_BF16, Uq, group, desc->m, desc->d, desc->r, desc->beta,
                                    Q, K_S, X, vmin, vmax, O, stream);
+  return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
+}
+
+size_t wildcat_decode_workspace_bytes(const wildcat_q_desc* desc) {
+  if (check_q(desc) != WILDCAT_OK) return 0;
+  return wc::DecodeLayout(desc->batch * desc->kv_heads, desc->m, desc->d, desc->r, desc->dtype == WILDCAT_BF16).total;
+}
+
+wildcat_status wildcat_decode(const wildcat_q_desc* desc, const void* Q, const void* K_S, const float* X,
+                              const float* vmin, const float* vmax, const void* K_new, const void* V_new, float* O,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const wildcat_status qs = check_q(desc);
+  if (qs != WILDCAT_OK) return qs;
+  if (!Q || !K_S || !X || !vmin || !vmax || !K_new || !V_new || !O) return WILDCAT_ERR_ARG;
+  if (!aligned16(Q) || !aligned16(K_S) || !aligned16(K_new) || !aligned16(V_new)) return WILDCAT_ERR_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < wildcat_decode_workspace_bytes(desc))
+    return WILDCAT_ERR_WORKSPACE;
+  const int Uq = desc->batch * desc->q_heads;
+  const int group = desc->q_heads / desc->kv_heads;
+  hipError_t e = wc::launch_decode(desc->dtype == WILDCAT_BF16, Uq, group, desc->m, desc->d, desc->r, desc->beta, Q,
+                                   K_S, X, vmin, vmax, K_new, V_new, O, workspace, stream);
   return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
 }
 

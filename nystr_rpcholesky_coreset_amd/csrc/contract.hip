@@ -23,6 +23,7 @@
 // vector ALU (expmm_bf16: from the bf16-rounded P; expmm32: from P in fp32
 // before rounding).  No running maximum is needed: the exponents are bounded
 // by the input-range contract.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -42,14 +43,23 @@ struct ContractArgs {
   const float* rowc;    // [units][rowsA] exponent offsets (weights + recentring) or null
   const float* colc;    // [unitsB][rowsB] exponent offsets (weights + recentring) or null
   float* out;           // weights: ypart [nsplit][units][rowsA][D+1]; attend: O [units][rowsA][D]
-  const float* vmin;    // attend: [unitsB][D]
+  const float* vmin;    // attend: [unitsB][D], or [unitsB][rowsA][D] with range_rows
   const float* vmax;
   int rowsA, rowsB;
   int chunk;            // right rows per split (weights); rowsB for attend
   int group;            // left unit u reads right unit u / group (GQA); 1 for weights
   int units;
   float scale;          // c (weights) or beta (attend)
+  // Attend over a cache with appended tokens: with `causal`, right row b >=
+  // causal_from is seen by left row a only when b - causal_from <= a.
+  int causal, causal_from;
+  int range_rows;       // attend: clip range per left row instead of per unit
 };
+
+// Right row b is visible to left row a (attend over a cache with appended tokens).
+__device__ __forceinline__ bool visible(const ContractArgs& p, int b, int a) {
+  return !p.causal || b - p.causal_from <= a;
+}
 
 enum { kModeWeights = 0, kModeAttend = 1 };
 
@@ -178,19 +188,16 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
         }
       }
       // bf16 P as the A operand of the value MFMA; extra column on the VALU.
+      // Attend: right rows past rowsB (staged as zeros) and rows hidden by
+      // the causal mask get P = 0.
       bf16x8 pfrag;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const __bf16 h = (__bf16)pv[j];
-        pfrag[j] = h;
         const int kk = 32 * kb + 8 * g + j;
+        const bool keep = MODE != kModeAttend || (b0 + kk < b_end && visible(p, b0 + kk, arow));
+        const __bf16 h = keep ? (__bf16)pv[j] : (__bf16)0.0f;
+        pfrag[j] = h;
         eacc = fmaf((float)h, sE[kk], eacc);
-      }
-      if (MODE == kModeAttend) {
-        // right rows past rowsB were staged as zeros; mask their P out
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (b0 + 32 * kb + 8 * g + j >= b_end) pfrag[j] = (__bf16)0.0f;
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -220,10 +227,12 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
   } else {
     float* O = p.out + (size_t)unit * p.rowsA * D;
     float lo[CT], hi[CT];   // read once: O stores could alias them
+    if (!p.range_rows) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      lo[ct] = p.vmin[(size_t)unitB * D + 16 * ct + r16];
-      hi[ct] = p.vmax[(size_t)unitB * D + 16 * ct + r16];
+      for (int ct = 0; ct < CT; ++ct) {
+        lo[ct] = p.vmin[(size_t)unitB * D + 16 * ct + r16];
+        hi[ct] = p.vmax[(size_t)unitB * D + 16 * ct + r16];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -231,6 +240,14 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
       const float e = __shfl(eacc, rl, 64);
       const int row = a0 + wave * 16 + rl;
       if (row < p.rowsA) {
+        if (p.range_rows) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const size_t k = ((size_t)unitB * p.rowsA + row) * D + 16 * ct + r16;
+            lo[ct] = p.vmin[k];
+            hi[ct] = p.vmax[k];
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const float x = oacc[ct][i] / e;
@@ -503,7 +520,10 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
       float arg = fmaf(sv[v], sc2, rc2);
       if (RC) arg += cv[v];
       float pv = __builtin_amdgcn_exp2f(arg);
-      if (MASKED) pv = (b0 + kofs + 16 * (v >> 3) + 8 * g2 + (v & 7) < b_end) ? pv : 0.0f;
+      if (MASKED) {
+        const int b = b0 + kofs + 16 * (v >> 3) + 8 * g2 + (v & 7);
+        pv = (b < b_end && (MODE != kModeAttend || visible(p, b, arow))) ? pv : 0.0f;
+      }
       const __bf16 h = (__bf16)pv;
       pfrag[v >> 3][v & 7] = h;
       eacc = MODE == kModeAttend ? fmaf(pv, ev[v], eacc) : eacc + pv;
@@ -542,7 +562,9 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
     constexpr bool PIPE = KS == 1;
     f32x16 s_next = {};
     if (PIPE) s_next = scores(buf, 0);
-    const bool full_tile = b0 + KT <= b_end;
+    // A tile takes the masked path if it runs past b_end or holds a right
+    // row that the causal mask hides from the wave's first left row.
+    const bool full_tile = b0 + KT <= b_end && (MODE != kModeAttend || visible(p, b0 + KT - 1, a0 + rw * 32));
 #pragma unroll
     for (int kb32 = 0; kb32 < KT / 32; ++kb32) {
       const f32x16 s_cur = PIPE ? s_next : scores(buf, 32 * kb32);
@@ -608,12 +630,15 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   } else {
     float* O = p.out + (size_t)unit * p.rowsA * D;
     // The lane's column bounds, read once (O stores could alias them, so
-    // reading inside the store loop would reload them after every store).
+    // reading inside the store loop would reload them after every store);
+    // per left row with range_rows.
     float lo[CT], hi[CT];
+    if (!p.range_rows) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      lo[ct] = p.vmin[(size_t)unitB * D + 32 * ct + r32];
-      hi[ct] = p.vmax[(size_t)unitB * D + 32 * ct + r32];
+      for (int ct = 0; ct < CT; ++ct) {
+        lo[ct] = p.vmin[(size_t)unitB * D + 32 * ct + r32];
+        hi[ct] = p.vmax[(size_t)unitB * D + 32 * ct + r32];
+      }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -621,6 +646,14 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
       const float e = __shfl(eacc, rl, 64);
       const int row = a0 + rw * 32 + rl;
       if (row < p.rowsA) {
+        if (p.range_rows) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const size_t k = ((size_t)unitB * p.rowsA + row) * D + 32 * ct + r32;
+            lo[ct] = p.vmin[k];
+            hi[ct] = p.vmax[k];
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
           O[(size_t)row * D + 32 * ct + r32] = fminf(fmaxf(oacc[ct][v] / e, lo[ct]), hi[ct]);
@@ -681,7 +714,8 @@ __global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
       float s = 0.0f;
 #pragma unroll
       for (int c = 0; c < D; ++c) s = fmaf(arow[c], sB[k][c], s);
-      const float pk = sE[k] != 0.0f ? expf(fmaf(s, p.scale, rc + sC[k])) : 0.0f;
+      const float pk = (sE[k] != 0.0f && (MODE != kModeAttend || visible(p, b0 + k, row)))
+                           ? expf(fmaf(s, p.scale, rc + sC[k])) : 0.0f;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = qc + 4 * j;
@@ -708,11 +742,12 @@ __global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
       const float e = sN[rl];
       float* O = p.out + ((size_t)unit * p.rowsA + row) * D;
       float lo[NC], hi[NC];   // read before any store: O stores could alias them
+      const size_t rbase = p.range_rows ? ((size_t)unitB * p.rowsA + row) * D : (size_t)unitB * D;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int c = qc + 4 * j;
-        lo[j] = c < D ? p.vmin[(size_t)unitB * D + c] : 0.0f;
-        hi[j] = c < D ? p.vmax[(size_t)unitB * D + c] : 0.0f;
+        lo[j] = c < D ? p.vmin[rbase + c] : 0.0f;
+        hi[j] = c < D ? p.vmax[rbase + c] : 0.0f;
       }
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
@@ -999,6 +1034,143 @@ hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, doubl
   a.A = Q; a.B = K_S; a.Vs = X; a.out = O; a.vmin = vmin; a.vmax = vmax;
   a.rowsA = m; a.rowsB = r; a.chunk = r; a.group = group; a.units = Uq;
   a.scale = (float)beta;
+  return launch_expmm_d<kModeAttend>(bf16 != 0, d, a, 1, st);
+}
+
+// ---- generation over a compressed cache --------------------------------
+// [WildCat, KV-cache paragraph: the compressed keys and values enter the
+// decoding phase through WtdAttn; m new tokens cost O(rmd + m^2 d).]
+// New token j joins the weighted attention as a weight-1 point with value
+// v_j, seen by the queries of tokens i >= j; the clip range of query i is
+// the cache's range widened by v_0 .. v_i.  The cache and the new tokens are
+// staged into one right operand ([K_S; K_new], [X; [V_new, 1]]) and attend
+// runs over it with the causal mask from row r and a clip range per row.
+
+// keys[u] = [K_S[u]; K_new[u]], xs[u] = [X[u]; [V_new[u], 1]].
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void decode_stage(const TK* K_S, const float* X, const TK* Kn, const TK* Vn,
+                                                       TK* keys, float* xs, int r, int m) {
+  const int u = blockIdx.y;
+  const int64_t R = (int64_t)r + m, stride = (int64_t)gridDim.x * kBlock;
+  const int64_t t0 = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  for (int64_t idx = t0; idx < R * (D + 1); idx += stride) {
+    const int64_t row = idx / (D + 1);
+    const int c = (int)(idx - row * (D + 1));
+    float x;
+    if (row < r) x = X[((size_t)u * r + row) * (D + 1) + c];
+    else x = c < D ? Elem<TK>::f32(Vn, ((size_t)u * m + (row - r)) * D + c) : 1.0f;
+    xs[(size_t)u * R * (D + 1) + idx] = x;
+  }
+  for (int64_t idx = t0; idx < R * D; idx += stride) {
+    const int64_t row = idx / D;
+    const int c = (int)(idx - row * D);
+    keys[(size_t)u * R * D + idx] =
+        row < r ? K_S[((size_t)u * r + row) * D + c] : Kn[((size_t)u * m + (row - r)) * D + c];
+  }
+}
+
+// The running clip range in three passes over blocks of kRangeRows new
+// values (fmin / fmax throughout: NaN values are skipped):
+//   range_blocks: bmin[u][b][c], bmax = column extremes of block b (b < nblk - 1);
+//   range_prefix: in place, bmin[u][b][c] = fmin(vmin[u][c], blocks 0 .. b);
+//   range_rows:   lo[u][i][c] = fmin(vmin[u][c], v_0c .. v_ic), hi likewise,
+//                 from the prefix of the blocks before row i's block.
+template <typename TK, int D>
+__global__ __launch_bounds__(D) void range_blocks(const TK* Vn, float* bmin, float* bmax, int m, int nblk) {
+  const int blk = blockIdx.x, u = blockIdx.y, c = threadIdx.x;
+  const int i0 = blk * kRangeRows, i1 = min(m, i0 + kRangeRows);
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = i0; i < i1; ++i) {
+    const float v = Elem<TK>::f32(Vn, ((size_t)u * m + i) * D + c);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  bmin[((size_t)u * nblk + blk) * D + c] = lo;
+  bmax[((size_t)u * nblk + blk) * D + c] = hi;
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void range_prefix(const float* vmin, const float* vmax, float* bmin, float* bmax,
+                                                  int nblk) {
+  const int u = blockIdx.x, c = threadIdx.x;
+  float lo = vmin[(size_t)u * D + c], hi = vmax[(size_t)u * D + c];
+  for (int b = 0; b + 1 < nblk; ++b) {
+    const size_t k = ((size_t)u * nblk + b) * D + c;
+    lo = fminf(lo, bmin[k]);
+    hi = fmaxf(hi, bmax[k]);
+    bmin[k] = lo;
+    bmax[k] = hi;
+  }
+}
+
+template <typename TK, int D>
+__global__ __launch_bounds__(D) void range_rows(const TK* Vn, const float* vmin, const float* vmax, const float* bmin,
+                                                const float* bmax, float* lo_out, float* hi_out, int m, int nblk) {
+  const int blk = blockIdx.x, u = blockIdx.y, c = threadIdx.x;
+  float lo, hi;
+  if (blk == 0) {
+    lo = vmin[(size_t)u * D + c];
+    hi = vmax[(size_t)u * D + c];
+  } else {
+    lo = bmin[((size_t)u * nblk + blk - 1) * D + c];
+    hi = bmax[((size_t)u * nblk + blk - 1) * D + c];
+  }
+  const int i0 = blk * kRangeRows, i1 = min(m, i0 + kRangeRows);
+  for (int i = i0; i < i1; ++i) {
+    const size_t k = ((size_t)u * m + i) * D + c;
+    const float v = Elem<TK>::f32(Vn, k);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+    lo_out[k] = lo;
+    hi_out[k] = hi;
+  }
+}
+
+template <typename TK, int D>
+static void launch_decode_prep(int Ukv, int m, int r, const void* K_S, const float* X, const void* Kn, const void* Vn,
+                               const float* vmin, const float* vmax, const DecodeLayout& lay, char* w,
+                               hipStream_t st) {
+  const int64_t items = ((int64_t)r + m) * (D + 1);
+  const int blocks = (int)std::min<int64_t>((items + kBlock - 1) / kBlock, 1024);
+  const TK* V = reinterpret_cast<const TK*>(Vn);
+  decode_stage<TK, D><<<dim3(blocks, Ukv), kBlock, 0, st>>>(
+      reinterpret_cast<const TK*>(K_S), X, reinterpret_cast<const TK*>(Kn), V, reinterpret_cast<TK*>(w + lay.keys),
+      reinterpret_cast<float*>(w + lay.xs), r, m);
+  float* bmin = reinterpret_cast<float*>(w + lay.bmin);
+  float* bmax = reinterpret_cast<float*>(w + lay.bmax);
+  if (lay.nblk > 1) {
+    range_blocks<TK, D><<<dim3(lay.nblk - 1, Ukv), D, 0, st>>>(V, bmin, bmax, m, lay.nblk);
+    range_prefix<D><<<Ukv, D, 0, st>>>(vmin, vmax, bmin, bmax, lay.nblk);
+  }
+  range_rows<TK, D><<<dim3(lay.nblk, Ukv), D, 0, st>>>(V, vmin, vmax, bmin, bmax, reinterpret_cast<float*>(w + lay.lo),
+                                                       reinterpret_cast<float*>(w + lay.hi), m, lay.nblk);
+}
+
+// Decode: O = clip(N[:, :d] / N[:, d]) with N_i = h(q_i, K_S) X + sum_{j<=i} h(q_i, k_j) [v_j, 1].
+hipError_t launch_decode(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
+                         const void* K_S, const float* X, const float* vmin, const float* vmax, const void* Kn,
+                         const void* Vn, float* O, void* ws, hipStream_t st) {
+  const int Ukv = Uq / group;
+  const DecodeLayout lay(Ukv, m, d, r, bf16 != 0);
+  char* w = static_cast<char*>(ws);
+#define WC_DECODE_PREP(TK, DD) launch_decode_prep<TK, DD>(Ukv, m, r, K_S, X, Kn, Vn, vmin, vmax, lay, w, st)
+  switch (d) {
+    case 16: if (bf16) WC_DECODE_PREP(bf16_t, 16); else WC_DECODE_PREP(float, 16); break;
+    case 32: if (bf16) WC_DECODE_PREP(bf16_t, 32); else WC_DECODE_PREP(float, 32); break;
+    case 64: if (bf16) WC_DECODE_PREP(bf16_t, 64); else WC_DECODE_PREP(float, 64); break;
+    case 128: if (bf16) WC_DECODE_PREP(bf16_t, 128); else WC_DECODE_PREP(float, 128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef WC_DECODE_PREP
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ContractArgs a{};
+  a.A = Q; a.B = w + lay.keys; a.Vs = w + lay.xs; a.out = O;
+  a.vmin = reinterpret_cast<const float*>(w + lay.lo);
+  a.vmax = reinterpret_cast<const float*>(w + lay.hi);
+  a.rowsA = m; a.rowsB = r + m; a.chunk = r + m; a.group = group; a.units = Uq;
+  a.scale = (float)beta;
+  a.causal = 1; a.causal_from = r; a.range_rows = 1;
   return launch_expmm_d<kModeAttend>(bf16 != 0, d, a, 1, st);
 }
 

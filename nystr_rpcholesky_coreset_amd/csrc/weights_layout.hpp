@@ -65,3 +65,30 @@ struct WeightsLayout {
 };
 
 }  // namespace wc
+
+namespace wc {
+
+// Decode workspace (generation over a compressed cache with m new tokens):
+//   keys    [U][r+m][d]       dtype  coreset keys, then the new tokens' keys
+//   xs      [U][r+m][d+1]     fp32   X, then [v_j, 1] for the new tokens
+//   lo, hi  [U][m][d]         fp32   running clip range of every new token
+//   bmin, bmax [U][nblk][d]   fp32   minima / maxima of blocks of kRangeRows new values
+constexpr int kRangeRows = 64;
+struct DecodeLayout {
+  int nblk;
+  size_t keys, xs, lo, hi, bmin, bmax, total;
+  DecodeLayout(int U, int m, int d, int r, bool bf16) {
+    const size_t R = (size_t)r + m;
+    nblk = (m + kRangeRows - 1) / kRangeRows;
+    size_t o = 0;
+    keys = o; o += al256((size_t)U * R * d * (bf16 ? 2 : 4));
+    xs = o;   o += al256((size_t)U * R * (d + 1) * 4);
+    lo = o;   o += al256((size_t)U * m * d * 4);
+    hi = o;   o += al256((size_t)U * m * d * 4);
+    bmin = o; o += al256((size_t)U * nblk * d * 4);
+    bmax = o; o += al256((size_t)U * nblk * d * 4);
+    total = o;
+  }
+};
+
+}  // namespace wc

@@ -42,8 +42,8 @@ WILDCAT_BF16 = 1
 
 EXPORTED = (
     "wildcat_select_workspace_bytes", "wildcat_weights_workspace_bytes", "wildcat_select",
-    "wildcat_weights", "wildcat_attend", "wildcat_merge_value_ranges", "wildcat_check_range",
-    "wildcat_status_string",
+    "wildcat_weights", "wildcat_attend", "wildcat_decode_workspace_bytes", "wildcat_decode",
+    "wildcat_merge_value_ranges", "wildcat_check_range", "wildcat_status_string",
 )
 
 
@@ -71,6 +71,11 @@ lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp,
 lib.wildcat_weights.restype = ctypes.c_int
 lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.wildcat_attend.restype = ctypes.c_int
+lib.wildcat_decode_workspace_bytes.argtypes = [ctypes.POINTER(QDesc)]
+lib.wildcat_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.wildcat_decode.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                               _vp]
+lib.wildcat_decode.restype = ctypes.c_int
 lib.wildcat_merge_value_ranges.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 lib.wildcat_merge_value_ranges.restype = ctypes.c_int
 lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
@@ -167,6 +172,25 @@ def attend(Q, K_S, X, vmin, vmax, beta, stream=None, out=None):
     O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
     _check(lib.wildcat_attend(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(O),
                               _stream(stream)), "wildcat_attend")
+    return O
+
+
+def decode_workspace_bytes(desc: QDesc) -> int:
+    return lib.wildcat_decode_workspace_bytes(ctypes.byref(desc))
+
+
+def decode(Q, K_S, X, vmin, vmax, K_new, V_new, beta, workspace=None, stream=None, out=None):
+    """wildcat_decode: the m new tokens (K_new, V_new [batch][kv_heads][m][d];
+    query row i of Q is token i's query) attend to the cache (K_S, X, vmin,
+    vmax) and causally to each other; returns O [batch][q_heads][m][d] float32."""
+    B, Hq, m, d = Q.shape
+    Hkv, r = K_S.shape[1], K_S.shape[2]
+    desc = QDesc(B, Hq, Hkv, m, d, r, float(beta), _dtype_code(Q))
+    O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
+    ws = _workspace(decode_workspace_bytes(desc), Q.device, workspace)
+    _check(lib.wildcat_decode(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(K_new),
+                              _ptr(V_new), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "wildcat_decode")
     return O
 
 

@@ -148,3 +148,42 @@ def test_merge_value_ranges_validation():
     assert mv(40000, 2, 64, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
     assert mv(8, 4, 128, None, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_ARG
     assert mv(8, 4, 128, FAKE, FAKE, FAKE, None, None) == wc.WILDCAT_ERR_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_heads=6, kv_heads=4), wc.WILDCAT_ERR_SHAPE),
+    (dict(d=48), wc.WILDCAT_ERR_SHAPE),
+    (dict(m=0), wc.WILDCAT_ERR_SHAPE),
+    (dict(r=0), wc.WILDCAT_ERR_SHAPE),
+    (dict(beta=float("inf")), wc.WILDCAT_ERR_ARG),
+    (dict(dtype=3), wc.WILDCAT_ERR_DTYPE),
+])
+def test_decode_rejects_bad_descriptors(kw, status):
+    q = _q(**kw)
+    assert wc.decode_workspace_bytes(q) == 0
+    assert wc.lib.wildcat_decode(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                 None) == status
+
+
+def test_decode_rejects_bad_pointers_and_small_workspace():
+    q = _q()
+    need = wc.decode_workspace_bytes(q)
+    # staged operand: U (r + m) (2d + 4(d+1)) bytes, plus the running ranges U m d 8
+    U, R = 2 * 4, 256 + 64
+    assert need >= U * R * (2 * 128 + 4 * 129) + U * 64 * 128 * 8
+    assert wc.decode_workspace_bytes(_q(m=128)) > need
+    args = [FAKE] * 9
+    for k in range(8):   # Q, K_S, X, vmin, vmax, K_new, V_new, O
+        a = list(args)
+        a[k] = None
+        assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_ARG
+    for k in (0, 1, 5, 6):   # Q, K_S, K_new, V_new are read with 16-byte loads
+        a = list(args)
+        a[k] = ctypes.c_void_p((1 << 20) + 4)
+        assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_ARG
+    assert wc.lib.wildcat_decode(ctypes.byref(q), *args, need - 1, None) == wc.WILDCAT_ERR_WORKSPACE
+    a = list(args)
+    a[8] = None
+    assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_WORKSPACE
+    a[8] = ctypes.c_void_p((1 << 20) + 8)
+    assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_WORKSPACE
