@@ -48,6 +48,13 @@ def contraction_flops(w, bins=1):
     return c1, c2
 
 
+def decode_flops(w):
+    """Flops of generation over the cache: query i of every head meets the r
+    cached points and new tokens 0..i, each with a score (2d) and a value
+    product (2(d+1))."""
+    return w.q_units * (4 * w.d + 2) * (w.m * w.r + w.m * (w.m + 1) // 2)
+
+
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "rpc_round_hbm_traffic_kvcache_n32768_r1024.md")
 
 
@@ -139,7 +146,7 @@ def main():
 
     w = I.WORKLOADS[args.workload]
     e = 2 if w.dtype == "bf16" else 4
-    inp = I.make_inputs(w)
+    inp = I.make_inputs(w, new_tokens=True)
     dev = torch.device("cuda:0")
 
     def to_dev(a):
@@ -177,7 +184,7 @@ def main():
         O = wc.attend(Q, K_S, X, vmin, vmax, w.beta)
         if ev:
             ev[3].record(stream)
-        return O, r_eff
+        return O, r_eff, (K_S, X, vmin, vmax)
 
     for _ in range(args.warmup):
         step()
@@ -187,7 +194,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        O, r_eff = step(evs[k])
+        O, r_eff, cache = step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ph = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(3)] for k in range(args.steps)])
@@ -196,6 +203,31 @@ def main():
     reff = r_eff.cpu().numpy()
     assert np.all(reff == rb), f"early stop on the bench workload: r_eff {reff}"
     assert torch.isfinite(O).all().item()
+
+    # generation over the compressed cache: the m new tokens of every kv head
+    # (query row i of each head is token i's query), after the timed steps
+    Kn, Vn = to_dev(inp["K_new"]), to_dev(inp["V_new"])
+    qd = wc.QDesc(w.batch, w.q_heads, w.kv_heads, w.m, w.d, w.r, float(w.beta), wc._dtype_code(Q))
+    ws_d = torch.empty(max(wc.decode_workspace_bytes(qd), 1), dtype=torch.uint8, device=dev)
+    Od = torch.empty_like(O)
+    wc.decode(Q, *cache, Kn, Vn, w.beta, workspace=ws_d, out=Od)
+    torch.cuda.synchronize()
+    dev_ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        wc.decode(Q, *cache, Kn, Vn, w.beta, workspace=ws_d, out=Od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dev_ms.append(e0.elapsed_time(e1))
+    t_dec = float(np.median(dev_ms))
+    assert torch.isfinite(Od).all().item()
+    f_dec = decode_flops(w)
+    peak = MFMA_BF16_TFLOPS if w.dtype == "bf16" else MFMA_FP32_TFLOPS
+    decode = {"new_tokens": w.m, "ms": t_dec, "rows_per_s": w.query_rows / (t_dec * 1e-3), "gflop": f_dec / 1e9,
+              "tflops": f_dec / (t_dec * 1e-3) / 1e12, "peak_tflops": peak,
+              "frac": f_dec / (t_dec * 1e-3) / 1e12 / peak}
+    del ws_d, Od, Kn, Vn
 
     if args.copy_calibration:
         a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
@@ -255,6 +287,7 @@ def main():
         "select_hbm_frac": sb / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "contraction_gflop": {"weights": c1 / 1e9, "attend": c2 / 1e9},
         "attend_only_rows_per_s": rows / (t_att * 1e-3),
+        "decode": decode,
         "exact_attention_gpu": exact,
         "roofline": {
             "kernel": "one RPNys round over all units" + (f" and their {B} bins" if B > 1 else "")

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(64 * NW) void expmm_bf16(ContractArgs p) {
   const int a0 = blockIdx.y * 16 * NW;
   const int split = blockIdx.x;
   const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
-  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  // causal: right rows hidden from every left row of the workgroup are skipped
+  if (MODE == kModeAttend && p.causal) b_end = min(b_end, p.causal_from + a0 + 16 * NW);
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (size_t)unit * p.rowsA * D;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (size_t)unitB * p.rowsB * D;
@@ -343,6 +345,9 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   const int split = blockIdx.x;
   int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
   int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  // causal: right rows hidden from every left row of the workgroup are
+  // skipped (not in the key-split form, whose waves share a barrier count)
+  if (KS == 1 && MODE == kModeAttend && p.causal) b_end = min(b_end, p.causal_from + a0 + 32 * Cfg::RW);
   int ntiles = (b_end - b_begin + KT - 1) / KT;
   if (KS > 1) {
     // Equal ranges of whole 32-row blocks; every wave runs the same number of
@@ -675,7 +680,8 @@ __global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
   const int unit = blockIdx.z, unitB = unit / p.group;
   const int a0 = blockIdx.y * kTileRows, split = blockIdx.x;
   const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
-  const int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
+  if (MODE == kModeAttend && p.causal) b_end = min(b_end, p.causal_from + a0 + kTileRows);
   const float* A = reinterpret_cast<const float*>(p.A) + (size_t)unit * p.rowsA * D;
   const float* B = reinterpret_cast<const float*>(p.B) + (size_t)unitB * p.rowsB * D;
   const int row = a0 + rl;
@@ -1046,35 +1052,13 @@ hipError_t launch_attend(int bf16, int Uq, int group, int m, int d, int r, doubl
 // staged into one right operand ([K_S; K_new], [X; [V_new, 1]]) and attend
 // runs over it with the causal mask from row r and a clip range per row.
 
-// keys[u] = [K_S[u]; K_new[u]], xs[u] = [X[u]; [V_new[u], 1]].
-template <typename TK, int D>
-__global__ __launch_bounds__(kBlock) void decode_stage(const TK* K_S, const float* X, const TK* Kn, const TK* Vn,
-                                                       TK* keys, float* xs, int r, int m) {
-  const int u = blockIdx.y;
-  const int64_t R = (int64_t)r + m, stride = (int64_t)gridDim.x * kBlock;
-  const int64_t t0 = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  for (int64_t idx = t0; idx < R * (D + 1); idx += stride) {
-    const int64_t row = idx / (D + 1);
-    const int c = (int)(idx - row * (D + 1));
-    float x;
-    if (row < r) x = X[((size_t)u * r + row) * (D + 1) + c];
-    else x = c < D ? Elem<TK>::f32(Vn, ((size_t)u * m + (row - r)) * D + c) : 1.0f;
-    xs[(size_t)u * R * (D + 1) + idx] = x;
-  }
-  for (int64_t idx = t0; idx < R * D; idx += stride) {
-    const int64_t row = idx / D;
-    const int c = (int)(idx - row * D);
-    keys[(size_t)u * R * D + idx] =
-        row < r ? K_S[((size_t)u * r + row) * D + c] : Kn[((size_t)u * m + (row - r)) * D + c];
-  }
-}
-
-// The running clip range in three passes over blocks of kRangeRows new
-// values (fmin / fmax throughout: NaN values are skipped):
+// The running clip range over blocks of kRangeRows new values (fmin / fmax
+// throughout: NaN values are skipped):
 //   range_blocks: bmin[u][b][c], bmax = column extremes of block b (b < nblk - 1);
 //   range_prefix: in place, bmin[u][b][c] = fmin(vmin[u][c], blocks 0 .. b);
-//   range_rows:   lo[u][i][c] = fmin(vmin[u][c], v_0c .. v_ic), hi likewise,
-//                 from the prefix of the blocks before row i's block.
+//   decode_prep (range role): lo[u][i][c] = fmin(vmin[u][c], v_0c .. v_ic), hi
+//                 likewise, from the prefix of the blocks before row i's block.
+// With m <= kRangeRows (one block) only decode_prep runs.
 template <typename TK, int D>
 __global__ __launch_bounds__(D) void range_blocks(const TK* Vn, float* bmin, float* bmax, int m, int nblk) {
   const int blk = blockIdx.x, u = blockIdx.y, c = threadIdx.x;
@@ -1103,26 +1087,95 @@ __global__ __launch_bounds__(D) void range_prefix(const float* vmin, const float
   }
 }
 
+constexpr int kPrepItems = 8;   // staged items per thread of decode_prep
+
+struct DecodePrepArgs {
+  const void *K_S, *Kn, *Vn;
+  const float *X, *vmin, *vmax, *bmin, *bmax;
+  void* keys;
+  float *xs, *lo, *hi;
+  int r, m, nblk, nstage;   // nstage: workgroups of the staging role
+};
+
+// One launch, two roles.  Workgroup b < nblk writes the running range of
+// block b of the new tokens (thread c: column c; the block's values are
+// loaded before the scan).  Workgroups nblk .. nblk + nstage - 1 stage the
+// operand: keys[u] = [K_S[u]; K_new[u]], xs[u] = [X[u]; [V_new[u], 1]].
 template <typename TK, int D>
-__global__ __launch_bounds__(D) void range_rows(const TK* Vn, const float* vmin, const float* vmax, const float* bmin,
-                                                const float* bmax, float* lo_out, float* hi_out, int m, int nblk) {
-  const int blk = blockIdx.x, u = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(kBlock) void decode_prep(DecodePrepArgs a) {
+  const int u = blockIdx.y, t = threadIdx.x;
+  const TK* Vn = reinterpret_cast<const TK*>(a.Vn);
+  if ((int)blockIdx.x >= a.nblk) {
+    // kPrepItems consecutive-by-thread items per thread; both candidate
+    // sources are loaded at clamped (valid) indices and the right one is
+    // selected, so no load waits behind a branch.
+    const TK* K_S = reinterpret_cast<const TK*>(a.K_S);
+    const TK* Kn = reinterpret_cast<const TK*>(a.Kn);
+    TK* keys = reinterpret_cast<TK*>(a.keys);
+    const int r = a.r, m = a.m;
+    const int64_t R = (int64_t)r + m;
+    const int64_t base = (int64_t)(blockIdx.x - a.nblk) * kBlock * kPrepItems + t;
+    const float* Xu = a.X + (size_t)u * r * (D + 1);
+    const TK* Vu = Vn + (size_t)u * m * D;
+    const int64_t nx = R * (D + 1), nk = R * D, xlast = (int64_t)r * (D + 1) - 1, vlast = (int64_t)m * D - 1;
+    float xv[kPrepItems];
+#pragma unroll
+    for (int k = 0; k < kPrepItems; ++k) {
+      const int64_t idx = base + (int64_t)k * kBlock;
+      const int64_t row = idx / (D + 1);
+      const int c = (int)(idx - row * (D + 1));
+      const float fx = Xu[std::min(std::max(idx, (int64_t)0), std::max(xlast, (int64_t)0))];
+      const float fv = Elem<TK>::f32(Vu, std::min(std::max((row - r) * D + c, (int64_t)0), vlast));
+      xv[k] = row < r ? fx : (c < D ? fv : 1.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < kPrepItems; ++k) {
+      const int64_t idx = base + (int64_t)k * kBlock;
+      if (idx < nx) a.xs[(size_t)u * R * (D + 1) + idx] = xv[k];
+    }
+    const TK* Ku = K_S + (size_t)u * r * D;
+    const TK* Knu = Kn + (size_t)u * m * D;
+    const int64_t klast = (int64_t)r * D - 1;
+    TK kv[kPrepItems];
+#pragma unroll
+    for (int k = 0; k < kPrepItems; ++k) {
+      const int64_t idx = base + (int64_t)k * kBlock;
+      const TK ks = Ku[std::min(std::max(idx, (int64_t)0), std::max(klast, (int64_t)0))];
+      const TK kn = Knu[std::min(std::max(idx - (int64_t)r * D, (int64_t)0), vlast)];
+      kv[k] = idx < (int64_t)r * D ? ks : kn;
+    }
+#pragma unroll
+    for (int k = 0; k < kPrepItems; ++k) {
+      const int64_t idx = base + (int64_t)k * kBlock;
+      if (idx < nk) keys[(size_t)u * R * D + idx] = kv[k];
+    }
+    return;
+  }
+  const int blk = blockIdx.x, c = t;
+  if (c >= D) return;
   float lo, hi;
   if (blk == 0) {
-    lo = vmin[(size_t)u * D + c];
-    hi = vmax[(size_t)u * D + c];
+    lo = a.vmin[(size_t)u * D + c];
+    hi = a.vmax[(size_t)u * D + c];
   } else {
-    lo = bmin[((size_t)u * nblk + blk - 1) * D + c];
-    hi = bmax[((size_t)u * nblk + blk - 1) * D + c];
+    lo = a.bmin[((size_t)u * a.nblk + blk - 1) * D + c];
+    hi = a.bmax[((size_t)u * a.nblk + blk - 1) * D + c];
   }
-  const int i0 = blk * kRangeRows, i1 = min(m, i0 + kRangeRows);
-  for (int i = i0; i < i1; ++i) {
-    const size_t k = ((size_t)u * m + i) * D + c;
-    const float v = Elem<TK>::f32(Vn, k);
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-    lo_out[k] = lo;
-    hi_out[k] = hi;
+  const int i0 = blk * kRangeRows, cnt = min(a.m - i0, kRangeRows);
+  // unconditional loads (rows past the end re-read the last row): a branch
+  // around each load would make every one wait for the previous
+  float v[kRangeRows];
+#pragma unroll
+  for (int j = 0; j < kRangeRows; ++j) v[j] = Elem<TK>::f32(Vn, ((size_t)u * a.m + i0 + min(j, cnt - 1)) * D + c);
+#pragma unroll
+  for (int j = 0; j < kRangeRows; ++j) {
+    if (j < cnt) {
+      const size_t k = ((size_t)u * a.m + i0 + j) * D + c;
+      lo = fminf(lo, v[j]);
+      hi = fmaxf(hi, v[j]);
+      a.lo[k] = lo;
+      a.hi[k] = hi;
+    }
   }
 }
 
@@ -1130,20 +1183,24 @@ template <typename TK, int D>
 static void launch_decode_prep(int Ukv, int m, int r, const void* K_S, const float* X, const void* Kn, const void* Vn,
                                const float* vmin, const float* vmax, const DecodeLayout& lay, char* w,
                                hipStream_t st) {
-  const int64_t items = ((int64_t)r + m) * (D + 1);
-  const int blocks = (int)std::min<int64_t>((items + kBlock - 1) / kBlock, 1024);
-  const TK* V = reinterpret_cast<const TK*>(Vn);
-  decode_stage<TK, D><<<dim3(blocks, Ukv), kBlock, 0, st>>>(
-      reinterpret_cast<const TK*>(K_S), X, reinterpret_cast<const TK*>(Kn), V, reinterpret_cast<TK*>(w + lay.keys),
-      reinterpret_cast<float*>(w + lay.xs), r, m);
+  DecodePrepArgs a{};
+  a.K_S = K_S; a.Kn = Kn; a.Vn = Vn; a.X = X; a.vmin = vmin; a.vmax = vmax;
   float* bmin = reinterpret_cast<float*>(w + lay.bmin);
   float* bmax = reinterpret_cast<float*>(w + lay.bmax);
+  a.bmin = bmin; a.bmax = bmax;
+  a.keys = w + lay.keys;
+  a.xs = reinterpret_cast<float*>(w + lay.xs);
+  a.lo = reinterpret_cast<float*>(w + lay.lo);
+  a.hi = reinterpret_cast<float*>(w + lay.hi);
+  a.r = r; a.m = m; a.nblk = lay.nblk;
+  const int64_t items = ((int64_t)r + m) * (D + 1);
+  a.nstage = (int)((items + kBlock * kPrepItems - 1) / (kBlock * kPrepItems));
   if (lay.nblk > 1) {
+    const TK* V = reinterpret_cast<const TK*>(Vn);
     range_blocks<TK, D><<<dim3(lay.nblk - 1, Ukv), D, 0, st>>>(V, bmin, bmax, m, lay.nblk);
     range_prefix<D><<<Ukv, D, 0, st>>>(vmin, vmax, bmin, bmax, lay.nblk);
   }
-  range_rows<TK, D><<<dim3(lay.nblk, Ukv), D, 0, st>>>(V, vmin, vmax, bmin, bmax, reinterpret_cast<float*>(w + lay.lo),
-                                                       reinterpret_cast<float*>(w + lay.hi), m, lay.nblk);
+  decode_prep<TK, D><<<dim3(lay.nblk + a.nstage, Ukv), kBlock, 0, st>>>(a);
 }
 
 // Decode: O = clip(N[:, :d] / N[:, d]) with N_i = h(q_i, K_S) X + sum_{j<=i} h(q_i, k_j) [v_j, 1].
