@@ -70,18 +70,28 @@ __device__ __forceinline__ void stage_inv_block(double* Td, const double* Dt) {
 // inverse block (TRANS: its transpose).  The current values go to Zt first
 // (one wave's LDS accesses execute in order), then each lane forms its row
 // of the product; the solved values are left in Zt for the panel update.
-template <int CPW, bool TRANS>
+template <int CPW, bool TRANS, int AB>
 __device__ __forceinline__ void apply_inv_block(const double* Td, double* Zt, double (&zq)[CPW], int lane, int nt) {
 #pragma unroll
   for (int c = 0; c < CPW; ++c) Zt[lane * CPW + c] = lane < nt ? zq[c] : 0.0;
   double acc[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) acc[c] = 0.0;
-#pragma unroll 8
-  for (int k = 0; k < 64; ++k) {
-    const double b = TRANS ? Td[dt_idx(k, lane)] : Td[dt_idx(lane, k)];
+  // batches of AB k: every LDS read of a batch is issued before its FMAs
+  // (same summation order, k = 0 .. 63)
+#pragma unroll 1
+  for (int k0 = 0; k0 < 64; k0 += AB) {
+    double b[AB], zk[AB][CPW];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) acc[c] = fma(b, Zt[k * CPW + c], acc[c]);
+    for (int k = 0; k < AB; ++k) {
+      b[k] = TRANS ? Td[dt_idx(k0 + k, lane)] : Td[dt_idx(lane, k0 + k)];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) zk[k][c] = Zt[(k0 + k) * CPW + c];
+    }
+#pragma unroll
+    for (int k = 0; k < AB; ++k)
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) acc[c] = fma(b[k], zk[k][c], acc[c]);
   }
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
@@ -126,6 +136,35 @@ __global__ __launch_bounds__(64) void invert_diag_blocks(const double* L, double
   for (int i = 0; i < 64; ++i) Du[i * 64 + j] = x[i];
 }
 
+// acc[c] = sum_{j < nt} panel[j * ld] * Zt[j][c], j in order.  A full tile
+// loads its 64 panel values in batches of PB, each issued before its FMAs,
+// so the loads overlap instead of waiting one after another (PB is bounded
+// by the registers a 1024-thread workgroup leaves per lane).
+template <int CPW, int PB>
+__device__ __forceinline__ void panel_dot(const double* panel, size_t ld, const double* Zt, int nt,
+                                          double (&acc)[CPW]) {
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) acc[c] = 0.0;
+  if (nt == 64) {
+#pragma unroll 1
+    for (int jb = 0; jb < 64; jb += PB) {
+      double lv[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) lv[j] = panel[(size_t)(jb + j) * ld];
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) acc[c] = fma(lv[j], Zt[(jb + j) * CPW + c], acc[c]);
+    }
+  } else {
+    for (int j = 0; j < nt; ++j) {
+      const double l = panel[(size_t)j * ld];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) acc[c] = fma(l, Zt[j * CPW + c], acc[c]);
+    }
+  }
+}
+
 constexpr int kXcds = 8;
 #ifndef WILDCAT_TRSM_XCD
 #define WILDCAT_TRSM_XCD 1   // place all column groups of a unit on one XCD
@@ -136,6 +175,8 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
                                                           const double* LT, const double* Dinv,
                                                           const int32_t* r_eff, float* X, int r,
                                                           int D1, int U, int G) {
+  constexpr int kPB = RPT >= 4 ? 8 : 16;   // panel loads per batch
+  constexpr int kAB = RPT >= 4 ? 4 : 8;    // inverse-block columns per batch
   __shared__ double Td[64 * 64];
   __shared__ double Zt[64 * CPW];
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
@@ -164,14 +205,13 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int c = 0; c < CPW; ++c)
-            part[k][c] = (sp0 + k < nsplit && c0 + c < D1)
-                             ? Yu[(size_t)(sp0 + k) * per_split + (size_t)i * D1 + c0 + c] : 0.0f;
+          for (int c = 0; c < CPW; ++c)   // clamped, unconditional loads (no wait behind a branch)
+            part[k][c] = Yu[(size_t)min(sp0 + k, nsplit - 1) * per_split + (size_t)i * D1 + min(c0 + c, D1 - 1)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
           for (int c = 0; c < CPW; ++c)
-            if (sp0 + k < nsplit) z[q][c] += (double)part[k][c];
+            if (sp0 + k < nsplit && c0 + c < D1) z[q][c] += (double)part[k][c];
       }
     }
   }
@@ -187,7 +227,7 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
       // index stays constant): z_t <- L_tt^{-1} z_t, lane = row.
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q == qo) apply_inv_block<CPW, false>(Td, Zt, z[q], lane, nt);
+        if (q == qo) apply_inv_block<CPW, false, kAB>(Td, Zt, z[q], lane, nt);
       }
     }
     __syncthreads();
@@ -196,14 +236,7 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
       const int i = t + q * NT;
       if (i >= i0 + nt && i < re) {
         double acc[CPW];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) acc[c] = 0.0;
-#pragma unroll 16
-        for (int j = 0; j < nt; ++j) {
-          const double l = LTu[(size_t)(i0 + j) * r + i];
-#pragma unroll
-          for (int c = 0; c < CPW; ++c) acc[c] = fma(l, Zt[j * CPW + c], acc[c]);
-        }
+        panel_dot<CPW, kPB>(LTu + (size_t)i0 * r + i, r, Zt, nt, acc);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) z[q][c] -= acc[c];
       }
@@ -221,7 +254,7 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
       // x_t <- L_tt^{-T} z_t.
 #pragma unroll
       for (int q = 0; q < RPT; ++q) {
-        if (q == qo) apply_inv_block<CPW, true>(Td, Zt, z[q], lane, nt);
+        if (q == qo) apply_inv_block<CPW, true, kAB>(Td, Zt, z[q], lane, nt);
       }
     }
     __syncthreads();
@@ -230,14 +263,7 @@ __global__ __launch_bounds__(NT) void trsm_cols(const float* ypart, int nsplit, 
       const int i = t + q * NT;
       if (i < i0) {
         double acc[CPW];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) acc[c] = 0.0;
-#pragma unroll 16
-        for (int j = 0; j < nt; ++j) {
-          const double l = Lu[(size_t)(i0 + j) * r + i];
-#pragma unroll
-          for (int c = 0; c < CPW; ++c) acc[c] = fma(l, Zt[j * CPW + c], acc[c]);
-        }
+        panel_dot<CPW, kPB>(Lu + (size_t)i0 * r + i, r, Zt, nt, acc);
 #pragma unroll
         for (int c = 0; c < CPW; ++c) z[q][c] -= acc[c];
       }
