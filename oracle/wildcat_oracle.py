@@ -107,7 +107,7 @@ class SelectResult:
     kernel_evals: int = 0    # number of h_tau entries evaluated
 
 
-def rpnys_select(K, u, r, beta, tau=1.0, recentre=False):
+def rpnys_select(K, u, r, beta, tau=1.0, recentre=False, factor="f64"):
     """Randomly pivoted partial Cholesky of H = h_tau(K, K).
 
     [WildCat, RPNys / Alg. 1 paragraph; Nystroem paragraph.]
@@ -125,7 +125,17 @@ def rpnys_select(K, u, r, beta, tau=1.0, recentre=False):
     the pivot stays positive until H is fully approximated.
 
     Only n + n*r_eff kernel entries are evaluated (the pages: O(nr) entries).
+
+    factor="f32" is the faster selection the pages leave to future work, in
+    the reading taken here: the factor is stored in float32 (each new column
+    is computed in float64 and rounded once), and everything else stays
+    float64 -- the kernel column, the products with the stored factor (exact
+    in float64), the sums, the draw.  The residual diagonal is downdated by
+    the square of the stored value, and L is taken from the stored values, so
+    the diagonal stays the residual of the stored factor.
     """
+    if factor not in ("f64", "f32"):
+        raise ValueError("factor must be 'f64' or 'f32'")
     Kc = prepare_keys(K, recentre)
     n = Kc.shape[0]
     u = np.asarray(u, dtype=np.float64)
@@ -145,6 +155,8 @@ def rpnys_select(K, u, r, beta, tau=1.0, recentre=False):
         if not (g[s] > 0):
             break
         F[i] = g / np.sqrt(g[s])
+        if factor == "f32":
+            F[i] = F[i].astype(np.float32).astype(np.float64)
         dres = np.maximum(dres - F[i] ** 2, 0.0)
         dres[s] = 0.0
         S.append(s)
@@ -339,12 +351,12 @@ class UnitResult:
     vmax: np.ndarray
 
 
-def compress_unit(K, V, u, r, beta, tau=1.0, recentre=False):
+def compress_unit(K, V, u, r, beta, tau=1.0, recentre=False, factor="f64"):
     """CompressKV for one (batch, kv-head): RPNys, then Nystroem weights.
 
-    [WildCat, CompressKV / Alg. 2 paragraph.]
+    [WildCat, CompressKV / Alg. 2 paragraph.]  factor: see rpnys_select.
     """
-    sel = rpnys_select(K, u, r, beta, tau, recentre)
+    sel = rpnys_select(K, u, r, beta, tau, recentre, factor)
     X, K_S = nystrom_weights(K, V, sel.S, sel.L, beta, tau, recentre)
     vmin, vmax = value_range(V)
     return UnitResult(sel=sel, X=X, K_S=K_S, vmin=vmin, vmax=vmax)
@@ -393,7 +405,7 @@ def compress_unit_binned(K, V, u, r, bins, beta, tau=1.0, recentre=False):
     return BinnedUnitResult(bins=parts, X=X, K_S=K_S, vmin=vmin, vmax=vmax)
 
 
-def wildcat_forward(Q, K, V, u, r, beta, tau=1.0, recentre=False):
+def wildcat_forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, factor="f64"):
     """WildCat over all units: Q [B][Hq][m][d], K, V [B][Hkv][n][d], u [B*Hkv][r].
 
     [WildCat, WildCat / Alg. 4 paragraph: CompressKV followed by WtdAttn.]
@@ -407,7 +419,7 @@ def wildcat_forward(Q, K, V, u, r, beta, tau=1.0, recentre=False):
     units = []
     for b in range(B):
         for h in range(Hkv):
-            units.append(compress_unit(K[b, h], V[b, h], u[b * Hkv + h], r, beta, tau, recentre))
+            units.append(compress_unit(K[b, h], V[b, h], u[b * Hkv + h], r, beta, tau, recentre, factor))
     O = np.empty((B, Hq, m, d))
     for b in range(B):
         for h in range(Hq):
