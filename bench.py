@@ -31,13 +31,14 @@ MFMA_BF16_TFLOPS = 2500.0
 MFMA_FP32_TFLOPS = 157.3
 
 
-def select_bytes(w, e, bins=1):
+def select_bytes(w, e, bins=1, fb=8):
     """Algorithmic HBM bytes of RPNys over all units (and bins): per unit (bin)
-    and round i the keys (n*d*e), the new factor column (8n), the residual
-    diagonal read and write (16n) and the previous factor columns (8*n*i),
-    with n/B keys and r/B rounds per bin."""
+    and round i the keys (n*d*e), the new factor column (fb*n), the residual
+    diagonal read and write (16n) and the previous factor columns (fb*n*i),
+    with n/B keys and r/B rounds per bin; fb = 8 (float64 factor) or 4
+    (float32 storage)."""
     U, n, d, r = w.units * bins, w.n // bins, w.d, w.r // bins
-    return U * n * (r * (d * e + 24) + 4 * r * (r - 1))
+    return U * n * (r * (d * e + 16 + fb) + fb * r * (r - 1) // 2)
 
 
 def contraction_flops(w, bins=1):
@@ -83,7 +84,7 @@ def measured_traffic(w):
         return None
 
 
-def cpu_baseline(w, inp, bins=1, target_s=20.0):
+def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
     """The oracle as it stands, timed on host cores on a bounded sample: whole
     kv units (select + weights + attend for their query heads), as many as fit
     in about target_s seconds (at least one)."""
@@ -103,9 +104,10 @@ def cpu_baseline(w, inp, bins=1, target_s=20.0):
     for uidx in range(w.units):
         b, h = divmod(uidx, w.kv_heads)
         if bins == 1:
-            ur = orc.compress_unit(K[b, h], V[b, h], inp["u"][uidx], w.r, w.beta, w.tau, w.recentre)
+            ur = orc.compress_unit(K[b, h], V[b, h], inp["u"][uidx], w.r, w.beta, w.tau, w.recentre, factor)
         else:
-            ur = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][uidx], w.r, bins, w.beta, w.tau, w.recentre)
+            ur = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][uidx], w.r, bins, w.beta, w.tau, w.recentre,
+                                          factor)
         for hq in range(h * group, (h + 1) * group):
             Q = I.to_f64(Qa[b, hq], w.dtype)
             orc.plugin_attend(Q, ur.K_S, ur.X, ur.vmin, ur.vmax, w.beta)
@@ -127,6 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--bins", type=int, default=1, help="key bins per kv head (1: plain RPNys)")
+    ap.add_argument("--factor", choices=("f64", "f32"), default="f64",
+                    help="storage of the RPNys factor (f32: the faster selection; all arithmetic stays fp64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain elementwise kernel over 1 GiB (1 GiB read + 1 GiB write), "
@@ -163,7 +167,7 @@ def main():
     rb = w.r // B
     Kb, Vb = (wc.bin_view(K, B), wc.bin_view(V, B)) if B > 1 else (K, V)
     ub = u.reshape(w.units * B, rb)
-    desc = wc.kv_desc(Kb, rb, w.beta, w.tau, w.recentre)
+    desc = wc.kv_desc(Kb, rb, w.beta, w.tau, w.recentre, args.factor)
     ws_sel = torch.empty(wc.select_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     ws_w = torch.empty(wc.weights_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -171,7 +175,7 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        S, r_eff, L = wc.select(Kb, ub, rb, w.beta, w.tau, w.recentre, workspace=ws_sel)
+        S, r_eff, L = wc.select(Kb, ub, rb, w.beta, w.tau, w.recentre, workspace=ws_sel, factor=args.factor)
         if ev:
             ev[1].record(stream)
         K_S, X, vmin, vmax = wc.weights(Kb, Vb, S, r_eff, L, rb, w.beta, w.tau, w.recentre, workspace=ws_w)
@@ -260,7 +264,8 @@ def main():
             continue
     del Ke, Ve
 
-    sb = select_bytes(w, e, B)
+    fb = 8 if args.factor == "f64" else 4
+    sb = select_bytes(w, e, B, fb)
     per_launch_bytes = sb / rb
     avg_launch_ms = t_sel / rb
     achieved = per_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
@@ -281,7 +286,8 @@ def main():
         "dtype": "f64+bf16" if w.dtype == "bf16" else "f64+fp32",
         "data": f"synthetic (seeded '{w.recipe}' recipe with the shapes of the {w.name} workload)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
-                   "n": w.n, "m": w.m, "d": w.d, "r": w.r, "bins": B, "beta": w.beta, "input_dtype": w.dtype},
+                   "n": w.n, "m": w.m, "d": w.d, "r": w.r, "bins": B, "beta": w.beta, "input_dtype": w.dtype,
+                   "factor": args.factor},
         "phases_ms": {"select": t_sel, "weights": t_wts, "attend": t_att},
         "rpcholesky_ms": t_sel,
         "select_hbm_frac": sb / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -298,14 +304,14 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(w) if B == 1 else None,
+            "traffic": measured_traffic(w) if B == 1 and args.factor == "f64" else None,
             "traffic_unit": "bytes per round (rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000)",
             "bytes_per_launch": per_launch_bytes,
             "avg_launch_ms": avg_launch_ms,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, B)
+        line["cpu_baseline"] = cpu_baseline(w, inp, B, factor=args.factor)
     print(json.dumps(line), flush=True)
 
 

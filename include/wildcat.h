@@ -78,10 +78,20 @@ typedef enum {
 
 typedef enum { WILDCAT_FP32 = 0, WILDCAT_BF16 = 1 } wildcat_dtype;
 
+/* Storage of the RPNys factor (wildcat_select only; all arithmetic is float64
+ * either way).  WILDCAT_FACTOR_F32 is the faster selection the pages leave to
+ * future work: each new factor column is computed in float64 and rounded once
+ * to float32 for storage, the residual diagonal is lowered by the square of
+ * the stored value and L holds the stored values.  It halves the bytes a round
+ * streams; the draws then follow the float32-stored factor, so they match the
+ * float64 mode's only while the decision margins exceed its perturbation. */
+typedef enum { WILDCAT_FACTOR_F64 = 0, WILDCAT_FACTOR_F32 = 1 } wildcat_factor;
+
 /* Keys/values of all units.  Ranges checked by every call:
  *   batch, kv_heads >= 1 and batch * kv_heads <= 65535;  1 <= n <= 2^21;
  *   d in {16, 32, 64, 128};  1 <= r <= min(n, 4096);  beta > 0 and tau > 0,
- *   both finite;  recentre in {0, 1};  dtype a wildcat_dtype (of K and V).
+ *   both finite;  recentre in {0, 1};  dtype a wildcat_dtype (of K and V);
+ *   factor a wildcat_factor (0, the float64 factor, when zero-initialised).
  * K, V, Q, K_S and the workspaces must be 16-byte aligned (WILDCAT_ERR_ARG,
  * or WILDCAT_ERR_WORKSPACE for a workspace, otherwise).                  */
 typedef struct {
@@ -91,6 +101,7 @@ typedef struct {
   double tau;         /* RPNys / weight kernel h_tau(k,k') = exp(beta <k,k'> / tau^2); 1 = h */
   int32_t recentre;   /* 1: keys minus their per-unit mean for select and weights */
   int32_t dtype;      /* wildcat_dtype of K and V */
+  int32_t factor;     /* wildcat_factor: storage of the RPNys factor */
 } wildcat_kv_desc;
 
 /* Queries.  q_heads a positive multiple of kv_heads, batch * q_heads <=
@@ -116,7 +127,9 @@ size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc);
  * positive residual from the end if rounding leaves none), evaluates
  * g = h_tau(K, k_s) - F[:, :i] F[s, :i]^T, sets column i of the factor to
  * g / sqrt(g_s), and lowers the residual diagonal by its square (zero at s).
- * All of this runs in float64, so the draws are reproducible bit for bit.
+ * All of this runs in float64, so the draws are reproducible bit for bit
+ * (desc->factor selects float64 or float32 storage of the factor, see
+ * wildcat_factor).
  *
  *   K          [U][n][d] dtype, read only.
  *   u          [U][r] float64 uniforms in [0, 1): the randomness, supplied by

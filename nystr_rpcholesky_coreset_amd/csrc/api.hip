@@ -6,7 +6,7 @@
 #include "weights_layout.hpp"
 
 namespace wc {
-hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
+hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre, int f32_factor, const void* K,
                          const double* u, int32_t* S, int32_t* r_eff, double* L, void* ws, hipStream_t st);
 hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
                           const void* V, const int32_t* S, const int32_t* r_eff, const double* L, void* K_S,
@@ -44,6 +44,7 @@ wildcat_status check_kv(const wildcat_kv_desc* k) {
   if (k->dtype != WILDCAT_FP32 && k->dtype != WILDCAT_BF16) return WILDCAT_ERR_DTYPE;
   if (!(isfinite(k->beta) && k->beta > 0.0) || !(isfinite(k->tau) && k->tau > 0.0)) return WILDCAT_ERR_ARG;
   if (k->recentre != 0 && k->recentre != 1) return WILDCAT_ERR_ARG;
+  if (k->factor != WILDCAT_FACTOR_F64 && k->factor != WILDCAT_FACTOR_F32) return WILDCAT_ERR_ARG;
   if (k->batch < 1 || k->kv_heads < 1 || k->n < 1 || k->n > wc::kMaxN || !valid_d(k->d)) return WILDCAT_ERR_SHAPE;
   if (k->r < 1 || k->r > k->n || k->r > wc::kMaxR) return WILDCAT_ERR_SHAPE;
   if ((int64_t)k->batch * k->kv_heads > 65535) return WILDCAT_ERR_SHAPE;
@@ -56,7 +57,8 @@ extern "C" {
 
 size_t wildcat_select_workspace_bytes(const wildcat_kv_desc* desc) {
   if (check_kv(desc) != WILDCAT_OK) return 0;
-  return wc::SelectLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r).total;
+  return wc::SelectLayout(desc->batch * desc->kv_heads, desc->n, desc->d, desc->r,
+                          desc->factor == WILDCAT_FACTOR_F32 ? 4 : 8).total;
 }
 
 size_t wildcat_weights_workspace_bytes(const wildcat_kv_desc* desc) {
@@ -75,6 +77,7 @@ wildcat_status wildcat_select(const wildcat_kv_desc* desc, const void* K, const 
   const int U = desc->batch * desc->kv_heads;
   const double c = desc->beta / (desc->tau * desc->tau);
   hipError_t e = wc::launch_select(desc->dtype == WILDCAT_BF16, U, desc->n, desc->d, desc->r, c, desc->recentre,
+                                   desc->factor == WILDCAT_FACTOR_F32,
                                    K, u, S, r_eff, L, workspace, stream);
   return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
 }
@@ -168,7 +171,7 @@ wildcat_status wildcat_merge_value_ranges(int32_t units, int32_t bins, int32_t d
 const char* wildcat_status_string(wildcat_status status) {
   switch (status) {
     case WILDCAT_OK: return "ok";
-    case WILDCAT_ERR_ARG: return "invalid argument (null or misaligned pointer, bad beta/tau/recentre)";
+    case WILDCAT_ERR_ARG: return "invalid argument (null or misaligned pointer, bad beta/tau/recentre/factor)";
     case WILDCAT_ERR_DTYPE: return "unsupported dtype";
     case WILDCAT_ERR_SHAPE: return "shape out of range";
     case WILDCAT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

@@ -46,7 +46,7 @@ struct SelectArgs {
   const double* u;      // [U][r]
   int32_t* S;           // [U][r]
   double* L;            // [U][r][r]
-  double* F;            // [U][nb][r][RB] (block-major factor)
+  void* F;              // [U][nb][r][RB] block-major factor, float64 or float32 (TF)
   double* dres;         // [U][npad]
   double* bsum;         // [U][nb]
   double* pivbuf;       // [U][2][pbs]
@@ -63,11 +63,19 @@ constexpr int RB = kSelRowsPerBlock;   // 128 rows per workgroup, 2 per lane of 
 constexpr double kStopRel = 1e-12;
 
 typedef double d2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 
-template <bool NT>
-__device__ __forceinline__ d2v ld2(const double* p) {
-  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const d2v*>(p));
-  return *reinterpret_cast<const d2v*>(p);
+// Two consecutive factor entries as float64: one 16-byte load of float64
+// storage, or one 8-byte load of float32 storage converted exactly.
+template <typename TF, bool NT>
+__device__ __forceinline__ d2v ldf(const TF* p) {
+  if constexpr (sizeof(TF) == 8) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const d2v*>(p));
+    return *reinterpret_cast<const d2v*>(p);
+  } else {
+    const f2v v = NT ? __builtin_nontemporal_load(reinterpret_cast<const f2v*>(p)) : *reinterpret_cast<const f2v*>(p);
+    return d2v{(double)v.x, (double)v.y};
+  }
 }
 
 // Key elements as float: chunks of 8 (one 16-byte load for bf16, two for
@@ -177,7 +185,7 @@ __device__ __forceinline__ double scan_block_totals(const SelectArgs& a, int u, 
 
 // Draw pivot i of unit u and stage it for the launch of round i.  Run by all
 // threads of one workgroup after round i-1 (or the initial diagonal).
-template <typename TK, int D, bool RC>
+template <typename TK, int D, bool RC, typename TF>
 __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, double* smem) {
   double* scr = smem;                              // 16 doubles
   int* iscr = reinterpret_cast<int*>(smem + 16);   // 8 ints
@@ -266,12 +274,12 @@ __device__ void draw_and_stage(const SelectArgs& a, int u, int i, bool is_init, 
     ks[c] = x;
     pb[2 + a.r + c] = x;
   }
-  const double* Fs = a.F + (((size_t)u * a.nb + s / RB) * a.r) * RB + (s % RB);
+  const TF* Fs = static_cast<const TF*>(a.F) + (((size_t)u * a.nb + s / RB) * a.r) * RB + (s % RB);
   double* Lrow = a.L + ((size_t)u * a.r + i) * a.r;
   double sq = 0.0;
   for (int j = t; j < a.r; j += kBlock) {
     if (j < i) {
-      const double f = Fs[(size_t)j * RB];
+      const double f = (double)Fs[(size_t)j * RB];
       pb[2 + j] = f;
       Lrow[j] = f;
       sq = fma(f, f, sq);
@@ -347,12 +355,12 @@ __global__ __launch_bounds__(kBlock) void rpc_init(SelectArgs a) {
 }
 
 // Pivot i of every running unit (one workgroup per unit).
-template <typename TK, int D, bool RC>
+template <typename TK, int D, bool RC, typename TF>
 __global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
   extern __shared__ double smem[];
   const int u = a.u0 + blockIdx.x;
   if (a.stopped[u]) return;
-  draw_and_stage<TK, D, RC>(a, u, i, i == 0, smem);
+  draw_and_stage<TK, D, RC, TF>(a, u, i, i == 0, smem);
 }
 
 // Tuning knobs of the streaming loop (compile-time).
@@ -368,7 +376,7 @@ static_assert(WILDCAT_SELECT_UNROLL % 4 == 0, "the factor loop consumes loads in
 #endif
 
 // One RPNys round i for the 128 keys of block blk of unit u.
-template <typename TK, int D, bool RC, bool NT>
+template <typename TK, int D, bool RC, bool NT, typename TF>
 __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, int blk, double* smem) {
   double* s_ks = smem + 32;              // D
   double* s_kbar = s_ks + D;             // D
@@ -391,21 +399,21 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
   const int row0 = blk * RB + lane * 2;
   const bool live = row0 < a.n;
   const bool has_y = row0 + 1 < a.n;
-  double* Fb = a.F + ((size_t)u * a.nb + blk) * a.r * RB;   // this workgroup's [r][RB] slab
+  TF* Fb = static_cast<TF*>(a.F) + ((size_t)u * a.nb + blk) * a.r * RB;   // this workgroup's [r][RB] slab
   constexpr size_t ld = RB;
 
   // This wave's quarter of sum_j F[j][l] F[s][j] for the lane's two rows.
   double fx = 0.0, fy = 0.0;
   if (live) {
     const int jb = (i * wave) >> 2, je = (i * (wave + 1)) >> 2;
-    const double* Fp = Fb + (size_t)jb * ld + 2 * lane;
+    const TF* Fp = Fb + (size_t)jb * ld + 2 * lane;
     double ax0 = 0.0, ay0 = 0.0, ax1 = 0.0, ay1 = 0.0, ax2 = 0.0, ay2 = 0.0, ax3 = 0.0, ay3 = 0.0;
     constexpr int UN = WILDCAT_SELECT_UNROLL;
     int j = jb;
     for (; j + UN <= je; j += UN) {
       d2v f[UN];
 #pragma unroll
-      for (int q = 0; q < UN; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
+      for (int q = 0; q < UN; ++q) f[q] = ldf<TF, NT>(Fp + (size_t)q * ld);
       Fp += UN * ld;
 #pragma unroll
       for (int q = 0; q < UN; q += 4) {
@@ -420,7 +428,7 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
     for (; j + 4 <= je; j += 4) {
       d2v f[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f[q] = ld2<NT>(Fp + (size_t)q * ld);
+      for (int q = 0; q < 4; ++q) f[q] = ldf<TF, NT>(Fp + (size_t)q * ld);
       Fp += 4 * ld;
       ax0 = fma(f[0].x, s_prow[j], ax0); ay0 = fma(f[0].y, s_prow[j], ay0);
       ax1 = fma(f[1].x, s_prow[j + 1], ax1); ay1 = fma(f[1].y, s_prow[j + 1], ay1);
@@ -428,7 +436,7 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
       ax3 = fma(f[3].x, s_prow[j + 3], ax3); ay3 = fma(f[3].y, s_prow[j + 3], ay3);
     }
     for (; j < je; ++j) {
-      const d2v f0 = ld2<NT>(Fp);
+      const d2v f0 = ldf<TF, NT>(Fp);
       Fp += ld;
       const double p0 = s_prow[j];
       ax0 = fma(f0.x, p0, ax0); ay0 = fma(f0.y, p0, ay0);
@@ -464,7 +472,15 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
       }
       fnew[0] = g[0] / sgs;
       fnew[1] = has_y ? g[1] / sgs : 0.0;
-      *reinterpret_cast<d2v*>(Fb + (size_t)i * ld + 2 * lane) = d2v{fnew[0], fnew[1]};
+      if constexpr (sizeof(TF) == 8) {
+        *reinterpret_cast<d2v*>(Fb + (size_t)i * ld + 2 * lane) = d2v{fnew[0], fnew[1]};
+      } else {
+        // float32 storage: round once; the downdate and L use the stored value
+        const f2v st = {(float)fnew[0], (float)fnew[1]};
+        *reinterpret_cast<f2v*>(Fb + (size_t)i * ld + 2 * lane) = st;
+        fnew[0] = (double)st.x;
+        fnew[1] = (double)st.y;
+      }
       const d2v dold = *reinterpret_cast<const d2v*>(du + row0);
       const double dd[2] = {dold.x, dold.y};
 #pragma unroll
@@ -486,10 +502,10 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
 }
 
 // One RPNys round i for every unit still running.
-template <typename TK, int D, bool RC, bool NT>
+template <typename TK, int D, bool RC, bool NT, typename TF>
 __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(SelectArgs a, int i) {
   extern __shared__ double smem[];
-  step_block<TK, D, RC, NT>(a, i, a.u0 + blockIdx.y, blockIdx.x, smem);
+  step_block<TK, D, RC, NT, TF>(a, i, a.u0 + blockIdx.y, blockIdx.x, smem);
 }
 
 // One launch of the paired schedule: the first ndraw workgroups draw pivot
@@ -497,18 +513,18 @@ __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_step(Sele
 // round si of group `sa` (nb workgroups per unit).  The two groups are
 // disjoint, so the roles touch disjoint data; the draw is the latency-bound
 // part and rides along with the other group's streaming.
-template <typename TK, int D, bool RC, bool NT>
+template <typename TK, int D, bool RC, bool NT, typename TF>
 __global__ __launch_bounds__(kBlock, WILDCAT_SELECT_MINWAVES) void rpc_fused(SelectArgs sa, int si, SelectArgs da,
                                                                              int di, int ndraw) {
   extern __shared__ double smem[];
   const int b = blockIdx.x;
   if (b < ndraw) {
     const int u = da.u0 + b;
-    if (!da.stopped[u]) draw_and_stage<TK, D, RC>(da, u, di, di == 0, smem);
+    if (!da.stopped[u]) draw_and_stage<TK, D, RC, TF>(da, u, di, di == 0, smem);
     return;
   }
   const int k = b - ndraw;
-  step_block<TK, D, RC, NT>(sa, si, sa.u0 + k / sa.nb, k % sa.nb, smem);
+  step_block<TK, D, RC, NT, TF>(sa, si, sa.u0 + k / sa.nb, k % sa.nb, smem);
 }
 
 // r_eff, -1 padding of S and zero rows of L past r_eff.
@@ -572,7 +588,7 @@ hipError_t aux_streams(AuxStreams** out) {
 }
 }  // namespace
 
-template <typename TK, int D, bool RC>
+template <typename TK, int D, bool RC, typename TF>
 static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hipStream_t st) {
   const dim3 grid(a.nb, U);
   rpc_clear<<<(U + kBlock - 1) / kBlock, kBlock, 0, st>>>(a, U);
@@ -615,15 +631,15 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
     // after its draw) is on an earlier launch of the same stream.
     for (int k = 0; k < NS; ++k) {
       SelectArgs both = ga[2 * k];   // the pair's units are contiguous
-      rpc_draw<TK, D, RC><<<gU[2 * k] + gU[2 * k + 1], kBlock, lds_draw, gs[k]>>>(both, 0);
+      rpc_draw<TK, D, RC, TF><<<gU[2 * k] + gU[2 * k + 1], kBlock, lds_draw, gs[k]>>>(both, 0);
     }
     for (int i = 0; i < a.r; ++i) {
       for (int k = 0; k < NS; ++k) {
         const int A = 2 * k, B = 2 * k + 1;
         const int nd1 = i >= 1 ? gU[B] : 0;
-        rpc_fused<TK, D, RC, NTL><<<nd1 + a.nb * gU[A], kBlock, lds_step, gs[k]>>>(ga[A], i, ga[B], i, nd1);
+        rpc_fused<TK, D, RC, NTL, TF><<<nd1 + a.nb * gU[A], kBlock, lds_step, gs[k]>>>(ga[A], i, ga[B], i, nd1);
         const int nd2 = i + 1 < a.r ? gU[A] : 0;
-        rpc_fused<TK, D, RC, NTL><<<nd2 + a.nb * gU[B], kBlock, lds_step, gs[k]>>>(ga[B], i, ga[A], i + 1, nd2);
+        rpc_fused<TK, D, RC, NTL, TF><<<nd2 + a.nb * gU[B], kBlock, lds_step, gs[k]>>>(ga[B], i, ga[A], i + 1, nd2);
       }
     }
     for (int k = 0; k < NS; ++k) {
@@ -631,11 +647,11 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
       rpc_finalize<<<gU[2 * k] + gU[2 * k + 1], kBlock, 0, gs[k]>>>(both, r_eff);
     }
   } else {
-    for (int g = 0; g < G; ++g) rpc_draw<TK, D, RC><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], 0);
+    for (int g = 0; g < G; ++g) rpc_draw<TK, D, RC, TF><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], 0);
     for (int i = 0; i < a.r; ++i) {
       for (int g = 0; g < G; ++g) {
-        rpc_step<TK, D, RC, NTL><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
-        if (i + 1 < a.r) rpc_draw<TK, D, RC><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], i + 1);
+        rpc_step<TK, D, RC, NTL, TF><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
+        if (i + 1 < a.r) rpc_draw<TK, D, RC, TF><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], i + 1);
       }
     }
     for (int g = 0; g < G; ++g) rpc_finalize<<<gU[g], kBlock, 0, gs[g]>>>(ga[g], r_eff);
@@ -649,30 +665,34 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
 }
 
 template <typename TK, int D>
-static hipError_t launch_select_rc(const SelectArgs& a, int U, bool rc, int32_t* r_eff, hipStream_t st) {
-  return rc ? launch_select_t<TK, D, true>(a, U, r_eff, st) : launch_select_t<TK, D, false>(a, U, r_eff, st);
+static hipError_t launch_select_rc(const SelectArgs& a, int U, bool rc, bool f32, int32_t* r_eff, hipStream_t st) {
+  if (f32) return rc ? launch_select_t<TK, D, true, float>(a, U, r_eff, st)
+                     : launch_select_t<TK, D, false, float>(a, U, r_eff, st);
+  return rc ? launch_select_t<TK, D, true, double>(a, U, r_eff, st)
+            : launch_select_t<TK, D, false, double>(a, U, r_eff, st);
 }
 
 template <typename TK>
-static hipError_t launch_select_d(const SelectArgs& a, int U, int d, bool rc, int32_t* r_eff, hipStream_t st) {
+static hipError_t launch_select_d(const SelectArgs& a, int U, int d, bool rc, bool f32, int32_t* r_eff,
+                                  hipStream_t st) {
   switch (d) {
-    case 16: return launch_select_rc<TK, 16>(a, U, rc, r_eff, st);
-    case 32: return launch_select_rc<TK, 32>(a, U, rc, r_eff, st);
-    case 64: return launch_select_rc<TK, 64>(a, U, rc, r_eff, st);
-    case 128: return launch_select_rc<TK, 128>(a, U, rc, r_eff, st);
+    case 16: return launch_select_rc<TK, 16>(a, U, rc, f32, r_eff, st);
+    case 32: return launch_select_rc<TK, 32>(a, U, rc, f32, r_eff, st);
+    case 64: return launch_select_rc<TK, 64>(a, U, rc, f32, r_eff, st);
+    case 128: return launch_select_rc<TK, 128>(a, U, rc, f32, r_eff, st);
   }
   return hipErrorInvalidValue;
 }
 
 // Host entry used by the C ABI (arguments already validated).
-hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre,
+hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int recentre, int f32_factor,
                          const void* K, const double* u, int32_t* S, int32_t* r_eff, double* L,
                          void* ws, hipStream_t st) {
-  const SelectLayout lay(U, n, d, r);
+  const SelectLayout lay(U, n, d, r, f32_factor ? 4 : 8);
   char* w = static_cast<char*>(ws);
   SelectArgs a;
   a.K = K; a.u = u; a.S = S; a.L = L;
-  a.F = reinterpret_cast<double*>(w + lay.F);
+  a.F = w + lay.F;
   a.dres = reinterpret_cast<double*>(w + lay.dres);
   a.bsum = reinterpret_cast<double*>(w + lay.bsum);
   a.pivbuf = reinterpret_cast<double*>(w + lay.pivbuf);
@@ -681,8 +701,8 @@ hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int rec
   a.stopped = reinterpret_cast<int32_t*>(w + lay.stopped);
   a.reff = reinterpret_cast<int32_t*>(w + lay.reff);
   a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.u0 = 0; a.c = c;
-  return bf16 ? launch_select_d<bf16_t>(a, U, d, recentre != 0, r_eff, st)
-              : launch_select_d<float>(a, U, d, recentre != 0, r_eff, st);
+  return bf16 ? launch_select_d<bf16_t>(a, U, d, recentre != 0, f32_factor != 0, r_eff, st)
+              : launch_select_d<float>(a, U, d, recentre != 0, f32_factor != 0, r_eff, st);
 }
 
 }  // namespace wc

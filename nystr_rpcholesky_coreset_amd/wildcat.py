@@ -50,7 +50,8 @@ EXPORTED = (
 class KVDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("beta", ctypes.c_double),
-                ("tau", ctypes.c_double), ("recentre", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("tau", ctypes.c_double), ("recentre", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("factor", ctypes.c_int32)]
 
 
 class QDesc(ctypes.Structure):
@@ -113,9 +114,15 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def kv_desc(K: torch.Tensor, r: int, beta: float, tau: float = 1.0, recentre: bool = False) -> KVDesc:
+FACTORS = {"f64": 0, "f32": 1}   # wildcat_factor: storage of the RPNys factor
+
+
+def kv_desc(K: torch.Tensor, r: int, beta: float, tau: float = 1.0, recentre: bool = False,
+            factor: str = "f64") -> KVDesc:
     B, H, n, d = K.shape
-    return KVDesc(B, H, n, d, int(r), float(beta), float(tau), int(bool(recentre)), _dtype_code(K))
+    if factor not in FACTORS:
+        raise ValueError(f"factor must be one of {sorted(FACTORS)}")
+    return KVDesc(B, H, n, d, int(r), float(beta), float(tau), int(bool(recentre)), _dtype_code(K), FACTORS[factor])
 
 
 def select_workspace_bytes(desc: KVDesc) -> int:
@@ -132,9 +139,10 @@ def _workspace(nbytes: int, device, workspace):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def select(K, u, r, beta, tau=1.0, recentre=False, workspace=None, stream=None):
-    """wildcat_select: returns (S [U][r] int32, r_eff [U] int32, L [U][r][r] float64)."""
-    desc = kv_desc(K, r, beta, tau, recentre)
+def select(K, u, r, beta, tau=1.0, recentre=False, workspace=None, stream=None, factor="f64"):
+    """wildcat_select: returns (S [U][r] int32, r_eff [U] int32, L [U][r][r] float64).
+    factor: "f64" or "f32" storage of the factor (wildcat_factor)."""
+    desc = kv_desc(K, r, beta, tau, recentre, factor)
     U = desc.batch * desc.kv_heads
     dev = K.device
     S = torch.empty((U, r), dtype=torch.int32, device=dev)
@@ -232,7 +240,7 @@ def bin_view(T, bins):
     return T.view(Bt, H * bins, n // bins, d)
 
 
-def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=None):
+def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=None, factor="f64"):
     """Binned WildCat: select and weights on the bin-major view (each bin an
     RPNys problem with r/bins pivots), per-unit value ranges, attend over the
     concatenated coreset.  Returns (O, parts); parts["S"] holds indices local
@@ -243,7 +251,7 @@ def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=No
     rb = r // bins
     Kb, Vb = bin_view(K, bins), bin_view(V, bins)
     ub = u.reshape(Bt * H * bins, rb)
-    S, r_eff, L = select(Kb, ub, rb, beta, tau, recentre, stream=stream)
+    S, r_eff, L = select(Kb, ub, rb, beta, tau, recentre, stream=stream, factor=factor)
     K_S, X, vmin_b, vmax_b = weights(Kb, Vb, S, r_eff, L, rb, beta, tau, recentre, stream=stream)
     vmin, vmax = merge_value_ranges(vmin_b, vmax_b, bins, stream=stream)
     K_S = K_S.view(Bt, H, r, d)
@@ -252,9 +260,9 @@ def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=No
     return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)
 
 
-def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None):
+def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None, factor="f64"):
     """WildCat module: select -> weights -> attend on one stream.  Returns (O, parts)."""
-    S, r_eff, L = select(K, u, r, beta, tau, recentre, stream=stream)
+    S, r_eff, L = select(K, u, r, beta, tau, recentre, stream=stream, factor=factor)
     K_S, X, vmin, vmax = weights(K, V, S, r_eff, L, r, beta, tau, recentre, stream=stream)
     O = attend(Q, K_S, X, vmin, vmax, beta, stream=stream)
     return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)

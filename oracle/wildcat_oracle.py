@@ -371,7 +371,7 @@ class BinnedUnitResult:
     vmax: np.ndarray
 
 
-def compress_unit_binned(K, V, u, r, bins, beta, tau=1.0, recentre=False):
+def compress_unit_binned(K, V, u, r, bins, beta, tau=1.0, recentre=False, factor="f64"):
     """Binned CompressKV for one unit.
 
     [WildCat, RPNys / Alg. 1 paragraph: the divide-and-conquer strategy that
@@ -398,7 +398,7 @@ def compress_unit_binned(K, V, u, r, bins, beta, tau=1.0, recentre=False):
         raise ValueError("n and r must be multiples of the number of bins")
     nb, rb = n // bins, r // bins
     parts = [compress_unit(K[b * nb:(b + 1) * nb], V[b * nb:(b + 1) * nb], u[b * rb:(b + 1) * rb], rb,
-                           beta, tau, recentre) for b in range(bins)]
+                           beta, tau, recentre, factor) for b in range(bins)]
     X = np.concatenate([p.X for p in parts], axis=0)
     K_S = np.concatenate([p.K_S for p in parts], axis=0)
     vmin, vmax = value_range(V)

@@ -36,7 +36,8 @@ FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fail
 
 
 def _kv(**kw):
-    base = dict(batch=2, kv_heads=4, n=5000, d=128, r=256, beta=0.1, tau=1.0, recentre=0, dtype=wc.WILDCAT_BF16)
+    base = dict(batch=2, kv_heads=4, n=5000, d=128, r=256, beta=0.1, tau=1.0, recentre=0, dtype=wc.WILDCAT_BF16,
+                factor=0)
     base.update(kw)
     return wc.KVDesc(*[base[f] for f, _ in wc.KVDesc._fields_])
 
@@ -64,6 +65,8 @@ def test_workspace_sizes_are_positive_and_grow_with_r():
     (dict(tau=-1.0), wc.WILDCAT_ERR_ARG),
     (dict(tau=float("inf")), wc.WILDCAT_ERR_ARG),
     (dict(recentre=2), wc.WILDCAT_ERR_ARG),
+    (dict(factor=2), wc.WILDCAT_ERR_ARG),
+    (dict(factor=-1), wc.WILDCAT_ERR_ARG),
 ])
 def test_select_rejects_bad_descriptors(kw, status):
     d = _kv(**kw)
@@ -187,3 +190,11 @@ def test_decode_rejects_bad_pointers_and_small_workspace():
     assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_WORKSPACE
     a[8] = ctypes.c_void_p((1 << 20) + 8)
     assert wc.lib.wildcat_decode(ctypes.byref(q), *a, need, None) == wc.WILDCAT_ERR_WORKSPACE
+
+
+def test_float32_factor_halves_the_factor_workspace():
+    a, b = wc.select_workspace_bytes(_kv(factor=0)), wc.select_workspace_bytes(_kv(factor=1))
+    U, npad, r = 8, 5120, 256
+    assert a - b >= U * r * npad * 4 - 512
+    assert b > U * r * npad * 4
+    assert wc.weights_workspace_bytes(_kv(factor=1)) == wc.weights_workspace_bytes(_kv(factor=0))
