@@ -56,10 +56,13 @@ def decode_flops(w):
     return w.q_units * (4 * w.d + 2) * (w.m * w.r + w.m * (w.m + 1) // 2)
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "rpc_round_hbm_traffic_kvcache_n32768_r1024.md")
+TRAFFIC_SUMMARY = {
+    "f64": os.path.join(ROOT, "profiles", "rpc_round_hbm_traffic_kvcache_n32768_r1024.md"),
+    "f32": os.path.join(ROOT, "profiles", "rpc_round_hbm_traffic_kvcache_n32768_r1024_f32factor.md"),
+}
 
 
-def measured_traffic(w):
+def measured_traffic(w, factor="f64"):
     """HBM bytes of one RPNys round measured with rocprofv3 FETCH_SIZE and
     WRITE_SIZE (calibrated on a plain 1 GiB elementwise kernel), read from the
     committed counter summary.  None unless that summary was taken on this
@@ -67,11 +70,11 @@ def measured_traffic(w):
     import hashlib
     try:
         fields = {}
-        for line in open(TRAFFIC_SUMMARY):
+        for line in open(TRAFFIC_SUMMARY[factor]):
             k, sep, v = line.strip().partition(": ")
             if sep:
                 fields[k] = v
-        if fields.get("workload") != w.name:
+        if fields.get("workload") != w.name or fields.get("factor") != factor:
             return None
         h = hashlib.sha256()
         for rel in fields["kernel_sources"].split():
@@ -304,7 +307,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(w) if B == 1 and args.factor == "f64" else None,
+            "traffic": measured_traffic(w, args.factor) if B == 1 else None,
             "traffic_unit": "bytes per round (rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000)",
             "bytes_per_launch": per_launch_bytes,
             "avg_launch_ms": avg_launch_ms,
