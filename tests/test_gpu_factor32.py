@@ -27,6 +27,9 @@ CASES = {
     "kv_gqa8x2_ragged": I.scaled_workload(C4, q_heads=8, kv_heads=2, n=5000, r=200, seed=54),
     "kv_recentre_tau": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=1500, r=100, recentre=True, tau=1.7, seed=55),
     "sphere_h2": I.scaled_workload(C5, q_heads=2, kv_heads=2, n=3000, m=400, r=150, seed=56),
+    # 64 units in eight unit groups
+    "units64_vit_n1000": I.scaled_workload(C2, batch=64, n=1000, m=30, r=50, seed=57),
+    "units64_latent_n2500": I.scaled_workload(C3, batch=8, q_heads=8, kv_heads=8, n=2500, m=30, r=40, seed=58),
 }
 
 

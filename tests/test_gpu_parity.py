@@ -37,6 +37,15 @@ SMALL_CASES = {
     "kv_keysplit_d128": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=3000, m=64, r=300, seed=21),
     "latent_keysplit_d64": I.scaled_workload(C3, batch=1, q_heads=2, kv_heads=2, n=2000, m=100, r=280, seed=22),
     "kv_keysplit_d32": I.scaled_workload(C4, q_heads=4, kv_heads=1, n=1200, m=50, r=260, d=32, seed=23),
+    # 64 or more units: eight unit groups of 8 or 9 units each on the paired
+    # streams, fp32 and bf16, recentring and tau, n up to 4096
+    "units64_vit_n600": I.scaled_workload(C2, batch=64, n=600, m=40, r=40, seed=24),
+    "units64_latent_n3000": I.scaled_workload(C3, batch=8, q_heads=8, kv_heads=8, n=3000, m=64, r=60, seed=25),
+    "units64_probe_fp32_recentre": I.scaled_workload(C1, batch=64, n=300, m=20, r=30, recentre=True, tau=0.9,
+                                                     seed=26),
+    "units64_kv_gqa_d128": I.scaled_workload(C4, batch=8, q_heads=16, kv_heads=8, n=1500, m=32, r=100, seed=27),
+    "units72_kv_n4096_tau": I.scaled_workload(C4, batch=9, q_heads=8, kv_heads=8, n=4096, m=16, r=48, tau=1.4,
+                                              seed=28),
 }
 
 
@@ -250,3 +259,28 @@ def test_concurrent_calls_on_two_streams_match_sequential():
     for k in range(2):
         for key in ("S", "r_eff", "L", "X", "O"):
             np.testing.assert_array_equal(out[k][key], ref[k][key])
+
+
+def test_many_units_mixed_early_stop():
+    """64 units in eight groups; every even unit u has only 3 + u % 7
+    distinct keys, so its residual vanishes after that many pivots and it
+    stops early (r_eff < r) while the others in its group run to r."""
+    rng = np.random.default_rng(31)
+    U, n, d, r = 64, 400, 32, 12
+    K = np.empty((U, n, d))
+    for u in range(U):
+        distinct = 3 + u % 7 if u % 2 == 0 else n
+        base = 0.3 * rng.standard_normal((min(distinct, n), d))
+        K[u] = base[rng.integers(0, len(base), n)] if distinct < n else 0.3 * rng.standard_normal((n, d))
+    V = rng.standard_normal((U, n, d))
+    Q = 0.3 * rng.standard_normal((U, 8, d))
+    w = I.Workload("units64_early", "unit_ball", U, 1, 1, 8, n, d, r, 0.5, "fp32", 0)
+    inp = {"Q": Q.astype(np.float32)[:, None], "K": K.astype(np.float32)[:, None], "V": V.astype(np.float32)[:, None],
+           "u": np.random.default_rng(32).random((U, r)), "workload": w}
+    g = _run_gpu(inp)
+    ref = oracle_units(inp, list(range(U)))
+    stopped = 0
+    for u in range(U):
+        _compare_unit(inp, g, u, ref[u])
+        stopped += int(g["r_eff"][u] < r)
+    assert stopped >= 16
