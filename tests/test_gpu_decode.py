@@ -26,6 +26,8 @@ C1, C2, C3, C4, C5 = (W[k] for k in I.WORKLOAD_ORDER)
 CASES = {
     "probe_fp32_d16": I.scaled_workload(C1, n=300, m=50, r=20, seed=31),
     "probe_fp32_d64_ragged": I.scaled_workload(C1, n=400, m=130, r=33, d=64, seed=32),
+    "probe_fp32_d128": I.scaled_workload(C1, q_heads=2, kv_heads=1, n=500, m=70, r=40, d=128, seed=43),
+    "probe_fp32_d32_m200": I.scaled_workload(C1, n=350, m=200, r=25, d=32, seed=44),
     "vit_b2_d64": I.scaled_workload(C2, batch=2, n=600, m=100, r=40, seed=33),
     "latent_m300": I.scaled_workload(C3, batch=1, q_heads=2, kv_heads=2, n=800, m=300, r=64, seed=34),
     "kv_gqa8x2_m64": I.scaled_workload(C4, q_heads=8, kv_heads=2, n=2000, m=64, r=200, seed=35),
