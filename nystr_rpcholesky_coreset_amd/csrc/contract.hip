@@ -555,9 +555,12 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   for (int it = 0; it < ntiles; ++it) {
     const int b0 = b_begin + it * KT;
     // Unconditional prefetch (the last tile re-loads itself into the idle
-    // buffer): keeps the loads out of branches so they stay in flight.
+    // buffer): keeps the loads out of branches so they stay in flight.  An
+    // attend over a single tile (few pivots, many query rows) has nothing to
+    // prefetch and skips it, and the staging and barrier after it.
+    const bool prefetch = MODE != kModeAttend || KS > 1 || ntiles > 1;
     const int bnext = it + 1 < ntiles ? b0 + KT : b0;
-    load_tile(bnext);
+    if (prefetch) load_tile(bnext);
 
     // Software pipeline over the tile's 32-row blocks: the score MFMAs of
     // block k+1 are issued before the probabilities of block k are computed,
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
       // Private single buffer: the wave's own reads of this tile were issued
       // before these stores, and one wave's LDS accesses execute in order.
       store_tile(0);
-    } else {
+    } else if (prefetch) {
       store_tile(buf ^ 1);
       __syncthreads();
       buf ^= 1;
