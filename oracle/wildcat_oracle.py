@@ -319,6 +319,24 @@ def decode_attend(Q, K_S, X, vmin, vmax, K_new, V_new, beta):
     return np.fmin(np.fmax(ratio, lo), hi)
 
 
+def decode_row(q, i, K_S, X, vmin, vmax, K_new, V_new, beta):
+    """Row i of decode_attend alone (query q of new token i), for sampling
+    outputs of long generations: the same definition restricted to one row,
+    touching only the cache and the new tokens 0 .. i."""
+    q = np.asarray(q, dtype=np.float64)[None, :]
+    d = q.shape[1]
+    Kn = np.asarray(K_new, dtype=np.float64)[:i + 1]
+    Vn = np.asarray(V_new, dtype=np.float64)[:i + 1]
+    N = query_kernel(q, np.asarray(K_S, dtype=np.float64).reshape(-1, d), beta) @ \
+        np.asarray(X, dtype=np.float64).reshape(-1, d + 1)
+    N = N + query_kernel(q, Kn, beta) @ np.hstack([Vn, np.ones((i + 1, 1))])
+    lo = np.fmin(np.asarray(vmin, dtype=np.float64), np.fmin.reduce(Vn, axis=0))
+    hi = np.fmax(np.asarray(vmax, dtype=np.float64), np.fmax.reduce(Vn, axis=0))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = N[0, :d] / N[0, d]
+    return np.fmin(np.fmax(ratio, lo), hi)
+
+
 def wildcat_decode(Q, K_S, X, vmin, vmax, K_new, V_new, beta):
     """decode_attend over all heads: Q [B][Hq][m][d]; K_S [B][Hkv][r][d];
     X [B][Hkv][r][d+1]; vmin, vmax [B][Hkv][d]; K_new, V_new [B][Hkv][m][d].

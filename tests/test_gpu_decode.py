@@ -164,3 +164,41 @@ def test_decode_after_gpu_compression_end_to_end():
     ref = _oracle(inp, K_S64, X32, vmn, vmx)
     scale = max(vscale, float(np.abs(I.to_f64(inp["V_new"], w.dtype)).max()))
     _check(O.cpu().numpy(), ref, scale, w.dtype, "end to end")
+
+
+def test_decode_long_context_sampled_rows():
+    """The 131k long-context workload's decode shape: 8 heads, a cache of
+    r = 2048 per head, m = 131072 new tokens attending causally (the
+    many-tile causal form, 2048 blocks of the running range).  The cache is a
+    seeded synthetic weighted coreset as above; sampled rows of two heads,
+    near the start, the middle and the end, are computed by the oracle one
+    by one."""
+    w = C5
+    print(f"[decode] long context: {w.name}: generating inputs", flush=True)
+    inp = I.make_inputs(w, new_tokens=True)
+    r = w.r
+    K_S = I.to_f64(inp["K"][:, :, :r], w.dtype)
+    V_S = I.to_f64(inp["V"][:, :, :r], w.dtype)
+    V = I.to_f64(inp["V"], w.dtype)
+    wt = np.random.default_rng(w.seed + 3000).uniform(0.5, 1.5, (w.batch, w.kv_heads, r, 1))
+    X = (wt * np.concatenate([V_S, np.ones_like(wt)], axis=3)).astype(np.float32)
+    vmin, vmax = V.min(axis=2).astype(np.float32), V.max(axis=2).astype(np.float32)
+    del V
+    print("[decode] long context: GPU", flush=True)
+    O = _run(inp, K_S, X, vmin, vmax)
+    assert np.all(np.isfinite(O))
+    Vn_all = I.to_f64(inp["V_new"], w.dtype)
+    scale = max(float(np.abs(V_S).max()), float(np.abs(Vn_all).max()), float(np.abs(vmin).max()),
+                float(np.abs(vmax).max()))
+    rows = [0, 1, 63, 64, 4097, 65535, 100000, w.m - 1]
+    worst = 0.0
+    for h in (0, 5):
+        Kn = I.to_f64(inp["K_new"][0, h], w.dtype)
+        Vn = Vn_all[0, h]
+        for i in rows:
+            q = I.to_f64(inp["Q"][0, h, i], w.dtype)
+            ref = orc.decode_row(q, i, K_S[0, h], X[0, h].astype(np.float64), vmin[0, h].astype(np.float64),
+                                 vmax[0, h].astype(np.float64), Kn, Vn, w.beta)
+            worst = max(worst, rel_max(O[0, h, i], ref, scale))
+    print(f"[decode] long context: max err {worst:.3e} of max|V|", flush=True)
+    assert worst < tol_for(w.dtype)

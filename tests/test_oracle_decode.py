@@ -11,7 +11,9 @@ oracle itself:
   * the clip takes the running range (closed-form cases with all kernel
     values equal to 1);
   * one new token is WtdAttn with that token appended as a weight-1 point;
-  * query head h reads kv head h // group.
+  * query head h reads kv head h // group;
+  * decode_row (one row, for sampling long generations) equals the
+    corresponding row of decode_attend.
 """
 import numpy as np
 import pytest
@@ -122,3 +124,14 @@ def test_query_heads_read_their_group():
             g = h // 2
             np.testing.assert_array_equal(
                 O[b, h], orc.decode_attend(Q[b, h], K_S[b, g], X[b, g], vmin[b, g], vmax[b, g], Kn[b, g], Vn[b, g], 0.5))
+
+
+def test_decode_row_matches_decode_attend():
+    Kp, Vp, Kn, Vn, Q = _tokens(12, 30, 17, 6)
+    rng = np.random.default_rng(13)
+    K_S, X = Kp[:9], np.hstack([rng.standard_normal((9, 6)), 0.5 + rng.random((9, 1))])
+    vmin, vmax = Vp.min(0), Vp.max(0)
+    O = orc.decode_attend(Q, K_S, X, vmin, vmax, Kn, Vn, 0.7)
+    for i in (0, 5, 16):
+        np.testing.assert_allclose(orc.decode_row(Q[i], i, K_S, X, vmin, vmax, Kn, Vn, 0.7), O[i],
+                                   rtol=1e-13, atol=1e-14)
