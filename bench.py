@@ -234,7 +234,24 @@ def main():
     decode = {"new_tokens": w.m, "ms": t_dec, "rows_per_s": w.query_rows / (t_dec * 1e-3), "gflop": f_dec / 1e9,
               "tflops": f_dec / (t_dec * 1e-3) / 1e12, "peak_tflops": peak,
               "frac": f_dec / (t_dec * 1e-3) / 1e12 / peak}
-    del ws_d, Od, Kn, Vn
+    # one new token per head (token-by-token generation): query row 0, token 0
+    Q1, Kn1, Vn1 = (x[:, :, :1].contiguous() for x in (Q, Kn, Vn))
+    qd1 = wc.QDesc(w.batch, w.q_heads, w.kv_heads, 1, w.d, w.r, float(w.beta), wc._dtype_code(Q))
+    ws_1 = torch.empty(max(wc.decode_workspace_bytes(qd1), 1), dtype=torch.uint8, device=dev)
+    O1 = torch.empty_like(Q1, dtype=torch.float32)
+    wc.decode(Q1, *cache, Kn1, Vn1, w.beta, workspace=ws_1, out=O1)
+    torch.cuda.synchronize()
+    tok_ms = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        wc.decode(Q1, *cache, Kn1, Vn1, w.beta, workspace=ws_1, out=O1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tok_ms.append(e0.elapsed_time(e1))
+    assert torch.isfinite(O1).all().item()
+    decode["one_token_us"] = float(np.median(tok_ms)) * 1e3
+    del ws_d, Od, Kn, Vn, Q1, Kn1, Vn1, ws_1, O1
 
     if args.copy_calibration:
         a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)

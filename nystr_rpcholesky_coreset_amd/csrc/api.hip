@@ -112,7 +112,8 @@ wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q, const v
 
 size_t wildcat_decode_workspace_bytes(const wildcat_q_desc* desc) {
   if (check_q(desc) != WILDCAT_OK) return 0;
-  return wc::DecodeLayout(desc->batch * desc->kv_heads, desc->m, desc->d, desc->r, desc->dtype == WILDCAT_BF16).total;
+  return wc::DecodeLayout(desc->batch * desc->kv_heads, desc->m, desc->d, desc->r, desc->dtype == WILDCAT_BF16,
+                          desc->batch * desc->q_heads).total;
 }
 
 wildcat_status wildcat_decode(const wildcat_q_desc* desc, const void* Q, const void* K_S, const float* X,

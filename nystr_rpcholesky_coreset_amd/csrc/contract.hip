@@ -1206,13 +1206,158 @@ static void launch_decode_prep(int Ukv, int m, int r, const void* K_S, const flo
   decode_prep<TK, D><<<dim3(lay.nblk + a.nstage, Ukv), kBlock, 0, st>>>(a);
 }
 
+// One new token (m = 1), the usual step of token-by-token generation: no
+// staging of the cache (the general form copies it into its operand and runs
+// a 32-row tile for one query row).  decode_one_part: workgroup (s, q-head)
+// takes key range s of the cache (one_token_split ranges of about 128 keys,
+// so the cache of a head is read by several CUs at once).  Phase 1: the
+// kernel values of its keys in fp32 (fp32 dot products of the exact inputs,
+// exp2), kept in LDS; range 0 also computes the new token's.  Phase 2: the
+// 256 threads split into D/4 column quads x 1024/D sub-ranges (16-byte loads
+// of X rows, which are 4-byte aligned; the weight column by the quad-0
+// threads); the sub-ranges' sums are added in order and written out.
+// decode_one_final: N = the ranges' sums in order + p_new [v_new, 1], then
+// O = clip(N[:d] / N[d]) with the range widened by v_new.
+template <typename TK, int D>
+__device__ __forceinline__ float dot_row(const TK* k, const float* sq) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if constexpr (std::is_same<TK, bf16_t>::value) {
+#pragma unroll
+    for (int c = 0; c < D; c += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(k + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __uint_as_float(w[j] << 16), x1 = __uint_as_float(w[j] & 0xFFFF0000u);
+        if (j & 1) { a2 = fmaf(x0, sq[c + 2 * j], a2); a3 = fmaf(x1, sq[c + 2 * j + 1], a3); }
+        else { a0 = fmaf(x0, sq[c + 2 * j], a0); a1 = fmaf(x1, sq[c + 2 * j + 1], a1); }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D; c += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(k + c);
+      a0 = fmaf(v.x, sq[c], a0); a1 = fmaf(v.y, sq[c + 1], a1);
+      a2 = fmaf(v.z, sq[c + 2], a2); a3 = fmaf(v.w, sq[c + 3], a3);
+    }
+  }
+  return (a0 + a1) + (a2 + a3);
+}
+
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void decode_one_part(const TK* Q, const TK* K_S, const float* X, const TK* Kn,
+                                                          float* part, float* pnew, int r, int group, int S,
+                                                          float scale2) {
+  constexpr int NQ = D / 4, NR = kBlock / NQ;   // column quads, sub-ranges
+  extern __shared__ float dsm[];
+  const int s = blockIdx.x, uq = blockIdx.y, u = uq / group, t = threadIdx.x;
+  const int k0 = (int)((int64_t)r * s / S), k1 = (int)((int64_t)r * (s + 1) / S), nk = k1 - k0;
+  float* sp = dsm;                              // nk kernel values
+  float* sq = dsm + ((nk + 3) & ~3);            // D query values
+  float* red = sq + D;                          // [NR][D + 1] sub-range sums
+  for (int c = t; c < D; c += kBlock) sq[c] = Elem<TK>::f32(Q, (size_t)uq * D + c);
+  __syncthreads();
+  for (int l = t; l < nk; l += kBlock) sp[l] = exp2f(dot_row<TK, D>(K_S + ((size_t)u * r + k0 + l) * D, sq) * scale2);
+  if (s == 0 && t == 0) pnew[uq] = exp2f(dot_row<TK, D>(Kn + (size_t)u * D, sq) * scale2);
+  __syncthreads();
+  const int cq = t % NQ, kr = t / NQ;
+  const int l0 = k0 + (int)((int64_t)nk * kr / NR), l1 = k0 + (int)((int64_t)nk * (kr + 1) / NR);
+  typedef float f4a __attribute__((ext_vector_type(4), aligned(4)));
+  const float* Xu = X + (size_t)u * r * (D + 1);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, accw = 0.f;
+  int l = l0;
+#pragma unroll 1
+  for (; l + 8 <= l1; l += 8) {
+    f4a x[8];
+    float xw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      x[q] = *reinterpret_cast<const f4a*>(Xu + (size_t)(l + q) * (D + 1) + 4 * cq);
+      xw[q] = Xu[(size_t)(l + q) * (D + 1) + D];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float p = sp[l + q - k0];
+      acc[0] = fmaf(p, x[q].x, acc[0]); acc[1] = fmaf(p, x[q].y, acc[1]);
+      acc[2] = fmaf(p, x[q].z, acc[2]); acc[3] = fmaf(p, x[q].w, acc[3]);
+      accw = fmaf(p, xw[q], accw);
+    }
+  }
+  for (; l < l1; ++l) {
+    const f4a x = *reinterpret_cast<const f4a*>(Xu + (size_t)l * (D + 1) + 4 * cq);
+    const float p = sp[l - k0];
+    acc[0] = fmaf(p, x.x, acc[0]); acc[1] = fmaf(p, x.y, acc[1]);
+    acc[2] = fmaf(p, x.z, acc[2]); acc[3] = fmaf(p, x.w, acc[3]);
+    accw = fmaf(p, Xu[(size_t)l * (D + 1) + D], accw);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[kr * (D + 1) + 4 * cq + j] = acc[j];
+  if (cq == 0) red[kr * (D + 1) + D] = accw;
+  __syncthreads();
+  for (int c = t; c <= D; c += kBlock) {
+    float n = 0.f;
+    for (int k = 0; k < NR; ++k) n += red[k * (D + 1) + c];
+    part[((size_t)uq * kOneSplit + s) * (D + 1) + c] = n;
+  }
+}
+
+template <typename TK, int D>
+__global__ __launch_bounds__(kBlock) void decode_one_final(const float* part, const float* pnew, const float* vmin,
+                                                           const float* vmax, const TK* Vn, float* O, int group,
+                                                           int S) {
+  __shared__ float sN[D + 1];
+  const int uq = blockIdx.x, u = uq / group, t = threadIdx.x;
+  for (int c = t; c <= D; c += kBlock) {
+    float n = 0.f;
+    for (int s = 0; s < S; ++s) n += part[((size_t)uq * kOneSplit + s) * (D + 1) + c];
+    const float vn = c < D ? Elem<TK>::f32(Vn, (size_t)u * D + c) : 1.0f;
+    sN[c] = fmaf(pnew[uq], vn, n);
+  }
+  __syncthreads();
+  for (int c = t; c < D; c += kBlock) {
+    const float vn = Elem<TK>::f32(Vn, (size_t)u * D + c);
+    const float lo = fminf(vmin[(size_t)u * D + c], vn), hi = fmaxf(vmax[(size_t)u * D + c], vn);
+    O[(size_t)uq * D + c] = fminf(fmaxf(sN[c] / sN[D], lo), hi);
+  }
+}
+
+template <typename TK, int D>
+static void launch_decode_one(int Uq, int group, int r, double beta, const void* Q, const void* K_S, const float* X,
+                              const float* vmin, const float* vmax, const void* Kn, const void* Vn, float* O,
+                              const DecodeLayout& lay, char* w, hipStream_t st) {
+  constexpr int NR = kBlock / (D / 4);
+  const int S = one_token_split(r);
+  const int nkmax = (r + S - 1) / S;
+  const size_t lds = (((nkmax + 3) & ~3) + D + NR * (D + 1)) * sizeof(float);
+  float* part = reinterpret_cast<float*>(w + lay.part);
+  float* pnew = reinterpret_cast<float*>(w + lay.pnew);
+  decode_one_part<TK, D><<<dim3(S, Uq), kBlock, lds, st>>>(
+      reinterpret_cast<const TK*>(Q), reinterpret_cast<const TK*>(K_S), X, reinterpret_cast<const TK*>(Kn), part, pnew,
+      r, group, S, (float)beta * kLog2e);
+  decode_one_final<TK, D><<<Uq, kBlock, 0, st>>>(part, pnew, vmin, vmax, reinterpret_cast<const TK*>(Vn), O, group,
+                                                 S);
+}
+
 // Decode: O = clip(N[:, :d] / N[:, d]) with N_i = h(q_i, K_S) X + sum_{j<=i} h(q_i, k_j) [v_j, 1].
 hipError_t launch_decode(int bf16, int Uq, int group, int m, int d, int r, double beta, const void* Q,
                          const void* K_S, const float* X, const float* vmin, const float* vmax, const void* Kn,
                          const void* Vn, float* O, void* ws, hipStream_t st) {
   const int Ukv = Uq / group;
-  const DecodeLayout lay(Ukv, m, d, r, bf16 != 0);
+  const DecodeLayout lay(Ukv, m, d, r, bf16 != 0, Uq);
   char* w = static_cast<char*>(ws);
+  if (m == 1) {
+#define WC_DECODE_ONE(TK, DD) \
+  launch_decode_one<TK, DD>(Uq, group, r, beta, Q, K_S, X, vmin, vmax, Kn, Vn, O, lay, w, st)
+    switch (d) {
+      case 16: if (bf16) WC_DECODE_ONE(bf16_t, 16); else WC_DECODE_ONE(float, 16); break;
+      case 32: if (bf16) WC_DECODE_ONE(bf16_t, 32); else WC_DECODE_ONE(float, 32); break;
+      case 64: if (bf16) WC_DECODE_ONE(bf16_t, 64); else WC_DECODE_ONE(float, 64); break;
+      case 128: if (bf16) WC_DECODE_ONE(bf16_t, 128); else WC_DECODE_ONE(float, 128); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef WC_DECODE_ONE
+    return hipGetLastError();
+  }
 #define WC_DECODE_PREP(TK, DD) launch_decode_prep<TK, DD>(Ukv, m, r, K_S, X, Kn, Vn, vmin, vmax, lay, w, st)
   switch (d) {
     case 16: if (bf16) WC_DECODE_PREP(bf16_t, 16); else WC_DECODE_PREP(float, 16); break;

@@ -68,19 +68,35 @@ struct WeightsLayout {
 
 namespace wc {
 
-// Decode workspace (generation over a compressed cache with m new tokens):
+// Decode workspace (generation over a compressed cache with m new tokens).
+// One new token (m = 1):
+//   part    [Uq][kOneSplit][d+1] fp32  partial sums of each query head's key ranges
+//   pnew    [Uq]                 fp32  kernel value of the new token
+// m > 1:
 //   keys    [U][r+m][d]       dtype  coreset keys, then the new tokens' keys
 //   xs      [U][r+m][d+1]     fp32   X, then [v_j, 1] for the new tokens
 //   lo, hi  [U][m][d]         fp32   running clip range of every new token
 //   bmin, bmax [U][nblk][d]   fp32   minima / maxima of blocks of kRangeRows new values
 constexpr int kRangeRows = 64;
+constexpr int kOneSplit = 8;      // most key ranges per query head for one new token
+constexpr int kOneKeys = 128;     // keys per range it aims at
+inline int one_token_split(int r) {
+  const int s = r / kOneKeys;
+  return s < 1 ? 1 : (s > kOneSplit ? kOneSplit : s);
+}
 struct DecodeLayout {
   int nblk;
-  size_t keys, xs, lo, hi, bmin, bmax, total;
-  DecodeLayout(int U, int m, int d, int r, bool bf16) {
+  size_t keys = 0, xs = 0, lo = 0, hi = 0, bmin = 0, bmax = 0, part = 0, pnew = 0, total;
+  DecodeLayout(int U, int m, int d, int r, bool bf16, int Uq) {
     const size_t R = (size_t)r + m;
     nblk = (m + kRangeRows - 1) / kRangeRows;
     size_t o = 0;
+    if (m == 1) {
+      part = o; o += al256((size_t)Uq * kOneSplit * (d + 1) * 4);
+      pnew = o; o += al256((size_t)Uq * 4);
+      total = o;
+      return;
+    }
     keys = o; o += al256((size_t)U * R * d * (bf16 ? 2 : 4));
     xs = o;   o += al256((size_t)U * R * (d + 1) * 4);
     lo = o;   o += al256((size_t)U * m * d * 4);

@@ -35,7 +35,11 @@ CASES = {
     "kv_d32_m70": I.scaled_workload(C4, q_heads=2, kv_heads=1, n=900, m=70, r=50, d=32, seed=37),
     "kv_d16_bf16": I.scaled_workload(C4, q_heads=2, kv_heads=1, n=700, m=90, r=60, d=16, seed=38),
     "sphere_m700": I.scaled_workload(C5, q_heads=2, kv_heads=2, n=1500, m=700, r=150, seed=39),
+    # one new token: the dedicated one-workgroup-per-query-head form
     "one_token": I.scaled_workload(C4, q_heads=4, kv_heads=2, n=800, m=1, r=100, seed=40),
+    "one_token_fp32_d16": I.scaled_workload(C1, n=300, m=1, r=25, seed=45),
+    "one_token_d64_b3": I.scaled_workload(C2, batch=3, n=500, m=1, r=60, seed=46),
+    "one_token_d32_r1": I.scaled_workload(C4, q_heads=2, kv_heads=1, n=200, m=1, r=1, d=32, seed=47),
     "rank_one": I.scaled_workload(C2, batch=1, n=300, m=40, r=1, seed=41),
 }
 
@@ -125,12 +129,14 @@ def test_decode_later_tokens_do_not_reach_earlier_queries():
     np.testing.assert_array_equal(_run(inp, K_S, X, vmin, vmax), base)
 
 
-def test_decode_full_size_kv_cache():
+@pytest.mark.parametrize("m", [64, 1])
+def test_decode_full_size_kv_cache(m):
     """The 32k KV-cache workload's decode shape: 32 query heads over 8 kv heads,
     a cache of r = 1024 per kv head, m = 64 new tokens (the key-split attend
-    kernel over 1088 rows).  The cache is a seeded synthetic weighted coreset:
-    K_S = the first r cached keys, X = w [V_S, 1] with weights w in [0.5, 1.5]."""
-    w = C4
+    kernel over 1088 rows) or one (the one-token form).  The cache is a seeded
+    synthetic weighted coreset: K_S = the first r cached keys, X = w [V_S, 1]
+    with weights w in [0.5, 1.5]."""
+    w = C4 if m == C4.m else I.scaled_workload(C4, m=m)
     print(f"[decode] full size: {w.name}", flush=True)
     inp = I.make_inputs(w, new_tokens=True)
     K = I.to_f64(inp["K"], w.dtype)
