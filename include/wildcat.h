@@ -211,7 +211,9 @@ wildcat_status wildcat_attend(const wildcat_q_desc* desc, const void* Q,
  *   O           [batch][q_heads][m][d] float32 out.
  *   workspace   >= wildcat_decode_workspace_bytes(desc) bytes, 16-byte
  *               aligned; contents on entry do not matter.  Holds the staged
- *               cache-plus-tokens operand and the running ranges.
+ *               cache-plus-tokens operand and the running ranges, or with
+ *               m = 1 (one new token: a form of its own, no staging) the
+ *               partial sums of each query head's key ranges.
  */
 size_t wildcat_decode_workspace_bytes(const wildcat_q_desc* desc);
 wildcat_status wildcat_decode(const wildcat_q_desc* desc, const void* Q,
