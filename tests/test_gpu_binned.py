@@ -14,7 +14,7 @@ sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 from nystr_rpcholesky_coreset_amd import inputs as I
 from oracle import wildcat_oracle as orc
 
-from _helpers import check_pivots, rel_max, to_device, tol_for
+from _helpers import NEAR_TIE, NEAR_TIE_F32, check_pivots, rel_max, to_device, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -31,20 +31,20 @@ CASES = {
 }
 
 
-def _run(inp, bins):
+def _run(inp, bins, factor="f64"):
     import torch
     from nystr_rpcholesky_coreset_amd import wildcat as wc
     w = inp["workload"]
     Q, K, V = (to_device(inp[k], w.dtype) for k in ("Q", "K", "V"))
     u = torch.from_numpy(inp["u"]).cuda()
-    O, parts = wc.forward_binned(Q, K, V, u, w.r, bins, w.beta, w.tau, w.recentre)
+    O, parts = wc.forward_binned(Q, K, V, u, w.r, bins, w.beta, w.tau, w.recentre, factor=factor)
     torch.cuda.synchronize()
     out = {k: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy() for k, v in parts.items()}
     out["O"] = O.cpu().numpy()
     return out
 
 
-def _compare(inp, g, bins, units):
+def _compare(inp, g, bins, units, factor="f64"):
     w = inp["workload"]
     K = I.to_f64(inp["K"], w.dtype)
     V = I.to_f64(inp["V"], w.dtype)
@@ -53,15 +53,17 @@ def _compare(inp, g, bins, units):
     group = w.q_heads // w.kv_heads
     for u in units:
         b, h = divmod(u, w.kv_heads)
-        res = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][u], w.r, bins, w.beta, w.tau, w.recentre)
+        res = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][u], w.r, bins, w.beta, w.tau, w.recentre,
+                                       factor)
         full = True
         for k, part in enumerate(res.bins):
             ub = u * bins + k
-            m = check_pivots(g["S"][ub], int(g["r_eff"][ub]), part.sel)
+            m = check_pivots(g["S"][ub], int(g["r_eff"][ub]), part.sel,
+                             near=NEAR_TIE if factor == "f64" else NEAR_TIE_F32)
             full &= m == part.sel.r_eff
             L = g["L"][ub]
             scale = max(1.0, float(np.abs(part.sel.L).max()))
-            assert rel_max(L[:m, :m], part.sel.L[:m, :m], scale) < 1e-9
+            assert rel_max(L[:m, :m], part.sel.L[:m, :m], scale) < (1e-9 if factor == "f64" else 2e-6)
             np.testing.assert_array_equal(g["K_S"][b, h][k * rb:k * rb + m], part.K_S[:m].astype(np.float32))
         np.testing.assert_array_equal(g["vmin"][b, h], res.vmin.astype(np.float32))
         np.testing.assert_array_equal(g["vmax"][b, h], res.vmax.astype(np.float32))
@@ -103,3 +105,13 @@ def test_binned_rejects_indivisible_sizes():
         wc.forward_binned(K[:, :, :, :], K, K, torch.zeros((1, 8), dtype=torch.float64, device="cuda"), 8, 3, 0.1)
     with pytest.raises(ValueError):   # n = 100 keys in 8 bins
         wc.forward_binned(K, K, K, torch.zeros((1, 8), dtype=torch.float64, device="cuda"), 8, 8, 0.1)
+
+
+@pytest.mark.parametrize("name", ["kv_b4", "vit_b8"])
+def test_binned_float32_factor(name):
+    """Binned selection with the float32 factor against the oracle's binned
+    float32-factor CompressKV."""
+    w, bins = CASES[name]
+    inp = I.make_inputs(w)
+    g = _run(inp, bins, factor="f32")
+    _compare(inp, g, bins, range(w.units), factor="f32")
