@@ -364,8 +364,11 @@ __global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
 }
 
 // Tuning knobs of the streaming loop (compile-time).
-#ifndef WILDCAT_SELECT_NT
-#define WILDCAT_SELECT_NT 1        // non-temporal factor loads (the factor is streamed once per round)
+#ifndef WILDCAT_SELECT_CACHED_BYTES
+// A round whose factor columns, over all units of the call, total at most this
+// many bytes reads them with ordinary loads, so the next round finds them in
+// the last-level cache; larger rounds stream them with non-temporal loads.
+#define WILDCAT_SELECT_CACHED_BYTES (256ull << 20)
 #endif
 #ifndef WILDCAT_SELECT_UNROLL
 #define WILDCAT_SELECT_UNROLL 12   // factor loads in flight per lane (8: 171.1 ms, 12: 169.9, 16: 170.6 on the 32k KV-cache workload)
@@ -622,7 +625,8 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
     ga[g].u0 = (int)((int64_t)U * g / G);
     gU[g] = (int)((int64_t)U * (g + 1) / G) - ga[g].u0;
   }
-  constexpr bool NTL = WILDCAT_SELECT_NT != 0;
+  const size_t col_bytes = (size_t)U * a.npad * (sizeof(TF));   // one factor column of every unit
+  auto cached = [&](int i) { return (size_t)i * col_bytes <= (size_t)WILDCAT_SELECT_CACHED_BYTES; };
   if (paired) {
     // Stream k runs groups A = 2k and B = 2k+1 alternately, each launch one
     // group's round together with the other group's next draw:
@@ -637,9 +641,14 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
       for (int k = 0; k < NS; ++k) {
         const int A = 2 * k, B = 2 * k + 1;
         const int nd1 = i >= 1 ? gU[B] : 0;
-        rpc_fused<TK, D, RC, NTL, TF><<<nd1 + a.nb * gU[A], kBlock, lds_step, gs[k]>>>(ga[A], i, ga[B], i, nd1);
         const int nd2 = i + 1 < a.r ? gU[A] : 0;
-        rpc_fused<TK, D, RC, NTL, TF><<<nd2 + a.nb * gU[B], kBlock, lds_step, gs[k]>>>(ga[B], i, ga[A], i + 1, nd2);
+        if (cached(i)) {
+          rpc_fused<TK, D, RC, false, TF><<<nd1 + a.nb * gU[A], kBlock, lds_step, gs[k]>>>(ga[A], i, ga[B], i, nd1);
+          rpc_fused<TK, D, RC, false, TF><<<nd2 + a.nb * gU[B], kBlock, lds_step, gs[k]>>>(ga[B], i, ga[A], i + 1, nd2);
+        } else {
+          rpc_fused<TK, D, RC, true, TF><<<nd1 + a.nb * gU[A], kBlock, lds_step, gs[k]>>>(ga[A], i, ga[B], i, nd1);
+          rpc_fused<TK, D, RC, true, TF><<<nd2 + a.nb * gU[B], kBlock, lds_step, gs[k]>>>(ga[B], i, ga[A], i + 1, nd2);
+        }
       }
     }
     for (int k = 0; k < NS; ++k) {
@@ -650,7 +659,8 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
     for (int g = 0; g < G; ++g) rpc_draw<TK, D, RC, TF><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], 0);
     for (int i = 0; i < a.r; ++i) {
       for (int g = 0; g < G; ++g) {
-        rpc_step<TK, D, RC, NTL, TF><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
+        if (cached(i)) rpc_step<TK, D, RC, false, TF><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
+        else rpc_step<TK, D, RC, true, TF><<<dim3(a.nb, gU[g]), kBlock, lds_step, gs[g]>>>(ga[g], i);
         if (i + 1 < a.r) rpc_draw<TK, D, RC, TF><<<gU[g], kBlock, lds_draw, gs[g]>>>(ga[g], i + 1);
       }
     }
