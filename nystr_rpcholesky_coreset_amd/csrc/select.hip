@@ -55,6 +55,7 @@ struct SelectArgs {
   int32_t* stopped;     // [U]
   int32_t* reff;        // [U]
   int n, npad, nb, r, pbs;
+  int jkeep;            // columns j < jkeep are read with ordinary loads in every round
   int u0;               // first unit of the launch (unit groups, see launch_select_t)
   double c;             // beta / tau^2
 };
@@ -370,6 +371,13 @@ __global__ __launch_bounds__(kBlock) void rpc_draw(SelectArgs a, int i) {
 // the last-level cache; larger rounds stream them with non-temporal loads.
 #define WILDCAT_SELECT_CACHED_BYTES (256ull << 20)
 #endif
+#ifndef WILDCAT_SELECT_KEEP_BYTES
+// In the larger rounds, the keys (read in every round with ordinary loads)
+// and the oldest factor columns share this much of the last-level cache: the
+// columns that fit beside the keys still take ordinary loads, so every round
+// finds them cached.  With the keys at or above it, no column is kept.
+#define WILDCAT_SELECT_KEEP_BYTES (224ull << 20)
+#endif
 #ifndef WILDCAT_SELECT_UNROLL
 #define WILDCAT_SELECT_UNROLL 12   // factor loads in flight per lane (8: 171.1 ms, 12: 169.9, 16: 170.6 on the 32k KV-cache workload)
 #endif
@@ -413,6 +421,27 @@ __device__ __forceinline__ void step_block(const SelectArgs& a, int i, int u, in
     double ax0 = 0.0, ay0 = 0.0, ax1 = 0.0, ay1 = 0.0, ax2 = 0.0, ay2 = 0.0, ax3 = 0.0, ay3 = 0.0;
     constexpr int UN = WILDCAT_SELECT_UNROLL;
     int j = jb;
+    if (NT) {
+      // The oldest columns (j < jkeep over all units of the call fit the
+      // last-level cache) take ordinary loads so they stay cached from round
+      // to round; whole chunks only, so the accumulation order is unchanged.
+      const int jk = a.jkeep < je ? a.jkeep : je;
+      const int jm = jk > jb ? jb + (jk - jb) / UN * UN : jb;
+      for (; j < jm; j += UN) {
+        d2v f[UN];
+#pragma unroll
+        for (int q = 0; q < UN; ++q) f[q] = ldf<TF, false>(Fp + (size_t)q * ld);
+        Fp += UN * ld;
+#pragma unroll
+        for (int q = 0; q < UN; q += 4) {
+          const double p0 = s_prow[j + q], p1 = s_prow[j + q + 1], p2 = s_prow[j + q + 2], p3 = s_prow[j + q + 3];
+          ax0 = fma(f[q].x, p0, ax0); ay0 = fma(f[q].y, p0, ay0);
+          ax1 = fma(f[q + 1].x, p1, ax1); ay1 = fma(f[q + 1].y, p1, ay1);
+          ax2 = fma(f[q + 2].x, p2, ax2); ay2 = fma(f[q + 2].y, p2, ay2);
+          ax3 = fma(f[q + 3].x, p3, ax3); ay3 = fma(f[q + 3].y, p3, ay3);
+        }
+      }
+    }
     for (; j + UN <= je; j += UN) {
       d2v f[UN];
 #pragma unroll
@@ -627,6 +656,12 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
   }
   const size_t col_bytes = (size_t)U * a.npad * (sizeof(TF));   // one factor column of every unit
   auto cached = [&](int i) { return (size_t)i * col_bytes <= (size_t)WILDCAT_SELECT_CACHED_BYTES; };
+  {
+    const size_t key_bytes = (size_t)U * a.n * D * sizeof(TK);
+    const size_t budget = (size_t)WILDCAT_SELECT_KEEP_BYTES;
+    const size_t keep = key_bytes < budget ? (budget - key_bytes) / col_bytes : 0;
+    for (int g = 0; g < G; ++g) ga[g].jkeep = (int)(keep < (size_t)a.r ? keep : (size_t)a.r);
+  }
   if (paired) {
     // Stream k runs groups A = 2k and B = 2k+1 alternately, each launch one
     // group's round together with the other group's next draw:
@@ -710,7 +745,7 @@ hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int rec
   a.kbar = reinterpret_cast<double*>(w + lay.kbar);
   a.stopped = reinterpret_cast<int32_t*>(w + lay.stopped);
   a.reff = reinterpret_cast<int32_t*>(w + lay.reff);
-  a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.u0 = 0; a.c = c;
+  a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.u0 = 0; a.jkeep = 0; a.c = c;
   return bf16 ? launch_select_d<bf16_t>(a, U, d, recentre != 0, f32_factor != 0, r_eff, st)
               : launch_select_d<float>(a, U, d, recentre != 0, f32_factor != 0, r_eff, st);
 }
