@@ -327,8 +327,8 @@ def main():
             "traffic": measured_traffic(w, args.factor) if B == 1 else None,
             "traffic_unit": "bytes per round (rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000)",
             "note": "achieved counts algorithmic bytes; the keys and the oldest factor columns "
-                    "(up to 224 MiB together) take ordinary loads and are partly served by the "
-                    "last-level cache, so the rate can pass what HBM alone delivers",
+                    "(up to 224 MiB together) take ordinary loads so that they can stay in the "
+                    "last-level cache from round to round",
             "bytes_per_launch": per_launch_bytes,
             "avg_launch_ms": avg_launch_ms,
         },
