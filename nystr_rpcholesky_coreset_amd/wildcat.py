@@ -27,7 +27,6 @@ LIB_PATH = os.environ.get("WILDCAT_LIBRARY") or os.path.join(_HERE, "libwildcat.
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nystr_rpcholesky_coreset_amd.build`")
 
-lib = ctypes.CDLL(LIB_PATH)
 
 WILDCAT_OK = 0
 WILDCAT_ERR_ARG = -1
@@ -61,29 +60,39 @@ class QDesc(ctypes.Structure):
 
 
 _vp = ctypes.c_void_p
-lib.wildcat_select_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
-lib.wildcat_select_workspace_bytes.restype = ctypes.c_size_t
-lib.wildcat_weights_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
-lib.wildcat_weights_workspace_bytes.restype = ctypes.c_size_t
-lib.wildcat_select.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-lib.wildcat_select.restype = ctypes.c_int
-lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                ctypes.c_size_t, _vp]
-lib.wildcat_weights.restype = ctypes.c_int
-lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-lib.wildcat_attend.restype = ctypes.c_int
-lib.wildcat_decode_workspace_bytes.argtypes = [ctypes.POINTER(QDesc)]
-lib.wildcat_decode_workspace_bytes.restype = ctypes.c_size_t
-lib.wildcat_decode.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
-                               _vp]
-lib.wildcat_decode.restype = ctypes.c_int
-lib.wildcat_merge_value_ranges.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
-lib.wildcat_merge_value_ranges.restype = ctypes.c_int
-lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
-                                    ctypes.POINTER(ctypes.c_double), _vp]
-lib.wildcat_check_range.restype = ctypes.c_int
-lib.wildcat_status_string.argtypes = [ctypes.c_int]
-lib.wildcat_status_string.restype = ctypes.c_char_p
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with the C signatures of
+    include/wildcat.h declared (the module's own `lib` is one)."""
+    lib = ctypes.CDLL(path)
+    lib.wildcat_select_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+    lib.wildcat_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.wildcat_weights_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+    lib.wildcat_weights_workspace_bytes.restype = ctypes.c_size_t
+    lib.wildcat_select.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.wildcat_select.restype = ctypes.c_int
+    lib.wildcat_weights.argtypes = [ctypes.POINTER(KVDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
+    lib.wildcat_weights.restype = ctypes.c_int
+    lib.wildcat_attend.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.wildcat_attend.restype = ctypes.c_int
+    lib.wildcat_decode_workspace_bytes.argtypes = [ctypes.POINTER(QDesc)]
+    lib.wildcat_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.wildcat_decode.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                   _vp]
+    lib.wildcat_decode.restype = ctypes.c_int
+    lib.wildcat_merge_value_ranges.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+    lib.wildcat_merge_value_ranges.restype = ctypes.c_int
+    lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
+                                        ctypes.POINTER(ctypes.c_double), _vp]
+    lib.wildcat_check_range.restype = ctypes.c_int
+    lib.wildcat_status_string.argtypes = [ctypes.c_int]
+    lib.wildcat_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = load_library(LIB_PATH)
 
 
 class WildcatError(RuntimeError):

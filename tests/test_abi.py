@@ -32,6 +32,20 @@ def test_library_exports_every_declared_function():
         assert hasattr(wc.lib, n), n
 
 
+def test_streamcheck_build_exports_the_same_functions():
+    """The test build with small cache thresholds (used by the GPU tests of the
+    factor-load paths) is the same library: it loads and exports every call,
+    and sizes workspaces identically."""
+    from nystr_rpcholesky_coreset_amd import build as B
+    assert os.path.exists(B.STREAMCHECK_LIB), "build with `python -m nystr_rpcholesky_coreset_amd.build`"
+    lib = wc.load_library(B.STREAMCHECK_LIB)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    desc = _kv()
+    assert lib.wildcat_select_workspace_bytes(ctypes.byref(desc)) == wc.lib.wildcat_select_workspace_bytes(
+        ctypes.byref(desc))
+
+
 FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
 
 
