@@ -418,8 +418,8 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
           int rp, c4;
           xitem(it, rp, c4);
           const int b = min(b0 + 2 * rp, blast), b1 = min(b0 + 2 * rp + 1, blast);
-          const f4u x = *reinterpret_cast<const f4u*>(X + (unsigned)(b * (D + 1) + 4 * c4));
-          const f4u y = *reinterpret_cast<const f4u*>(X + (unsigned)(b1 * (D + 1) + 4 * c4));
+          const f4u x = *reinterpret_cast<const f4u*>(X + ((size_t)b * (D + 1) + 4 * c4));
+          const f4u y = *reinterpret_cast<const f4u*>(X + ((size_t)b1 * (D + 1) + 4 * c4));
           xreg[8 * q] = x.x; xreg[8 * q + 1] = x.y; xreg[8 * q + 2] = x.z; xreg[8 * q + 3] = x.w;
           xreg[8 * q + 4] = y.x; xreg[8 * q + 5] = y.y; xreg[8 * q + 6] = y.z; xreg[8 * q + 7] = y.w;
         }

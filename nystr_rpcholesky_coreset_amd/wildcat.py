@@ -14,6 +14,7 @@ Shapes (row-major, head dim fastest):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -123,6 +124,14 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocations made inside belong to the stream the kernels run on, so the
+    caching allocator does not hand their memory to work on another stream
+    while those kernels may still use it (a workspace is released when the
+    call returns, before the kernels have finished)."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 FACTORS = {"f64": 0, "f32": 1}   # wildcat_factor: storage of the RPNys factor
 
 
@@ -154,13 +163,14 @@ def select(K, u, r, beta, tau=1.0, recentre=False, workspace=None, stream=None, 
     desc = kv_desc(K, r, beta, tau, recentre, factor)
     U = desc.batch * desc.kv_heads
     dev = K.device
-    S = torch.empty((U, r), dtype=torch.int32, device=dev)
-    r_eff = torch.empty((U,), dtype=torch.int32, device=dev)
-    L = torch.empty((U, r, r), dtype=torch.float64, device=dev)
-    nbytes = select_workspace_bytes(desc)
-    ws = _workspace(nbytes, dev, workspace)
-    _check(lib.wildcat_select(ctypes.byref(desc), _ptr(K), _ptr(u), _ptr(S), _ptr(r_eff), _ptr(L),
-                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "wildcat_select")
+    with _on(stream):
+        S = torch.empty((U, r), dtype=torch.int32, device=dev)
+        r_eff = torch.empty((U,), dtype=torch.int32, device=dev)
+        L = torch.empty((U, r, r), dtype=torch.float64, device=dev)
+        nbytes = select_workspace_bytes(desc)
+        ws = _workspace(nbytes, dev, workspace)
+        _check(lib.wildcat_select(ctypes.byref(desc), _ptr(K), _ptr(u), _ptr(S), _ptr(r_eff), _ptr(L),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "wildcat_select")
     return S, r_eff, L
 
 
@@ -169,15 +179,16 @@ def weights(K, V, S, r_eff, L, r, beta, tau=1.0, recentre=False, workspace=None,
     desc = kv_desc(K, r, beta, tau, recentre)
     B, H, n, d = K.shape
     dev = K.device
-    K_S = torch.empty((B, H, r, d), dtype=K.dtype, device=dev)
-    X = torch.empty((B, H, r, d + 1), dtype=torch.float32, device=dev)
-    vmin = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    vmax = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    nbytes = weights_workspace_bytes(desc)
-    ws = _workspace(nbytes, dev, workspace)
-    _check(lib.wildcat_weights(ctypes.byref(desc), _ptr(K), _ptr(V), _ptr(S), _ptr(r_eff), _ptr(L), _ptr(K_S),
-                               _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(ws), ws.numel() * ws.element_size(),
-                               _stream(stream)), "wildcat_weights")
+    with _on(stream):
+        K_S = torch.empty((B, H, r, d), dtype=K.dtype, device=dev)
+        X = torch.empty((B, H, r, d + 1), dtype=torch.float32, device=dev)
+        vmin = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+        vmax = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+        nbytes = weights_workspace_bytes(desc)
+        ws = _workspace(nbytes, dev, workspace)
+        _check(lib.wildcat_weights(ctypes.byref(desc), _ptr(K), _ptr(V), _ptr(S), _ptr(r_eff), _ptr(L), _ptr(K_S),
+                                   _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "wildcat_weights")
     return K_S, X, vmin, vmax
 
 
@@ -186,7 +197,8 @@ def attend(Q, K_S, X, vmin, vmax, beta, stream=None, out=None):
     B, Hq, m, d = Q.shape
     Hkv, r = K_S.shape[1], K_S.shape[2]
     desc = QDesc(B, Hq, Hkv, m, d, r, float(beta), _dtype_code(Q))
-    O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
+    with _on(stream):
+        O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
     _check(lib.wildcat_attend(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(O),
                               _stream(stream)), "wildcat_attend")
     return O
@@ -203,11 +215,12 @@ def decode(Q, K_S, X, vmin, vmax, K_new, V_new, beta, workspace=None, stream=Non
     B, Hq, m, d = Q.shape
     Hkv, r = K_S.shape[1], K_S.shape[2]
     desc = QDesc(B, Hq, Hkv, m, d, r, float(beta), _dtype_code(Q))
-    O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
-    ws = _workspace(decode_workspace_bytes(desc), Q.device, workspace)
-    _check(lib.wildcat_decode(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax), _ptr(K_new),
-                              _ptr(V_new), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "wildcat_decode")
+    with _on(stream):
+        O = out if out is not None else torch.empty((B, Hq, m, d), dtype=torch.float32, device=Q.device)
+        ws = _workspace(decode_workspace_bytes(desc), Q.device, workspace)
+        _check(lib.wildcat_decode(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax),
+                                  _ptr(K_new), _ptr(V_new), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "wildcat_decode")
     return O
 
 
@@ -220,10 +233,11 @@ def check_range(K, r, beta, tau=1.0, recentre=False, Q=None, scratch=None, strea
     if Q is not None:
         B, Hq, m, d = Q.shape
         qd = QDesc(B, Hq, K.shape[1], m, d, int(r), float(beta), _dtype_code(Q))
-    buf = scratch if scratch is not None else torch.empty(2, dtype=torch.float64, device=K.device)
-    bounds = (ctypes.c_double * 2)()
-    st = lib.wildcat_check_range(ctypes.byref(desc), _ptr(K), ctypes.byref(qd) if qd is not None else None,
-                                 _ptr(Q), _ptr(buf), bounds, _stream(stream))
+    with _on(stream):
+        buf = scratch if scratch is not None else torch.empty(2, dtype=torch.float64, device=K.device)
+        bounds = (ctypes.c_double * 2)()
+        st = lib.wildcat_check_range(ctypes.byref(desc), _ptr(K), ctypes.byref(qd) if qd is not None else None,
+                                     _ptr(Q), _ptr(buf), bounds, _stream(stream))
     if st != WILDCAT_OK:
         raise WildcatError(st, "wildcat_check_range",
                            f": E_k = {bounds[0]:.4g}, E_q = {bounds[1]:.4g}" if st == WILDCAT_ERR_RANGE else "")
@@ -234,8 +248,9 @@ def merge_value_ranges(vmin_bins, vmax_bins, bins, stream=None):
     """wildcat_merge_value_ranges: [B][H*bins][d] per-bin ranges -> [B][H][d]."""
     Bt, HB, d = vmin_bins.shape
     H = HB // bins
-    vmin = torch.empty((Bt, H, d), dtype=torch.float32, device=vmin_bins.device)
-    vmax = torch.empty_like(vmin)
+    with _on(stream):
+        vmin = torch.empty((Bt, H, d), dtype=torch.float32, device=vmin_bins.device)
+        vmax = torch.empty_like(vmin)
     _check(lib.wildcat_merge_value_ranges(Bt * H, bins, d, _ptr(vmin_bins), _ptr(vmax_bins), _ptr(vmin), _ptr(vmax),
                                           _stream(stream)), "wildcat_merge_value_ranges")
     return vmin, vmax

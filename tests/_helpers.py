@@ -60,16 +60,26 @@ def oracle_attend_rows(inp: dict, unit_res, qunit: int, rows=None):
 NEAR_TIE_F32 = 1e-6
 
 
-def check_pivots(S_gpu: np.ndarray, reff_gpu: int, sel, near: float = NEAR_TIE) -> int:
+# Every draw at which a comparison stopped on a near tie, as
+# (context, draw, margin): printed in the session summary (conftest.py), so a
+# shortened comparison is always visible.
+NEAR_TIE_EXITS: list = []
+
+
+def check_pivots(S_gpu: np.ndarray, reff_gpu: int, sel, near: float = NEAR_TIE, context: str = "") -> int:
     """Pivots must match the oracle bit for bit.  A mismatch is accepted only
     at a step whose oracle decision margin is below `near` (a near tie); then
-    the comparison stops there.  Returns the matched length."""
+    the comparison stops there and the exit is recorded in NEAR_TIE_EXITS.
+    Returns the matched length (sel.r_eff when everything matched)."""
     n_or = sel.r_eff
     k = min(n_or, reff_gpu)
     for i in range(k):
         if int(S_gpu[i]) != int(sel.S[i]):
             assert sel.margins[i] < near, (
                 f"pivot {i}: gpu {S_gpu[i]} vs oracle {sel.S[i]} with decision margin {sel.margins[i]:.3e}")
+            NEAR_TIE_EXITS.append((context, i, float(sel.margins[i])))
+            print(f"near tie {context}: pivots diverge at draw {i} (margin {sel.margins[i]:.3e}); "
+                  f"comparison stops there", flush=True)
             return i
     assert reff_gpu == n_or, f"r_eff gpu {reff_gpu} vs oracle {n_or}"
     assert np.all(S_gpu[reff_gpu:] == -1)

@@ -44,7 +44,7 @@ def _run(inp, bins, factor="f64"):
     return out
 
 
-def _compare(inp, g, bins, units, factor="f64"):
+def _compare(inp, g, bins, units, factor="f64", allow_near_tie=True):
     w = inp["workload"]
     K = I.to_f64(inp["K"], w.dtype)
     V = I.to_f64(inp["V"], w.dtype)
@@ -59,8 +59,10 @@ def _compare(inp, g, bins, units, factor="f64"):
         for k, part in enumerate(res.bins):
             ub = u * bins + k
             m = check_pivots(g["S"][ub], int(g["r_eff"][ub]), part.sel,
-                             near=NEAR_TIE if factor == "f64" else NEAR_TIE_F32)
+                             near=NEAR_TIE if factor == "f64" else NEAR_TIE_F32,
+                             context=f"{w.name} bins {bins} {factor} unit {u} bin {k}")
             full &= m == part.sel.r_eff
+            assert m == part.sel.r_eff or allow_near_tie, f"unit {u} bin {k}: a near tie at draw {m}"
             L = g["L"][ub]
             scale = max(1.0, float(np.abs(part.sel.L).max()))
             assert rel_max(L[:m, :m], part.sel.L[:m, :m], scale) < (1e-9 if factor == "f64" else 2e-6)
@@ -94,7 +96,7 @@ def test_binned_kvcache_fullsize_all_units():
     inp = I.make_inputs(w)
     g = _run(inp, 4)
     print("running the oracle on all 8 units x 4 bins", flush=True)
-    _compare(inp, g, 4, range(w.units))
+    _compare(inp, g, 4, range(w.units), allow_near_tie=False)
 
 
 def test_binned_rejects_indivisible_sizes():

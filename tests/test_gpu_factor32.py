@@ -57,7 +57,7 @@ def _oracle_unit(inp, u):
 def _compare(inp, g, u, ures):
     w = inp["workload"]
     sel = ures.sel
-    matched = check_pivots(g["S"][u], int(g["r_eff"][u]), sel, near=NEAR_TIE_F32)
+    matched = check_pivots(g["S"][u], int(g["r_eff"][u]), sel, near=NEAR_TIE_F32, context=f"{w.name} f32 unit {u}")
     L = g["L"][u]
     np.testing.assert_array_equal(L[:matched, :matched], L[:matched, :matched].astype(np.float32))
     assert rel_max(L[:matched, :matched], sel.L[:matched, :matched], max(1.0, float(np.abs(sel.L).max()))) < 2e-6
@@ -111,3 +111,4 @@ def test_factor32_full_size_kv_cache_unit():
     print("oracle on unit 5", flush=True)
     matched = _compare(inp, g, 5, _oracle_unit(inp, 5))
     print(f"unit 5: {matched} of {w.r} pivots match the oracle", flush=True)
+    assert matched == w.r, "a near tie stopped the full-size comparison short"

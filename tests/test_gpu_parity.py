@@ -3,9 +3,11 @@
 Oracle-sized cases compare every output element by element; they span several
 workgroups of the selection kernel (512 keys each) with ragged tails, several
 64-row contraction tiles, GQA groups, recentring and tau != 1.  Pivots must
-match bit for bit (a mismatch is tolerated only at an fp64 near tie, see
-_helpers.check_pivots), L to 1e-9 of its scale, the value range exactly, and
-O within 2e-3 (fp32) or 2e-2 (bf16) of max|V|.
+match bit for bit, L to 1e-9 of its scale, the value range exactly, and O
+within 2e-3 (fp32) or 2e-2 (bf16) of max|V|.  A pivot mismatch at an fp64 near
+tie (see _helpers.check_pivots) would stop the comparison of that unit short;
+it fails the test unless the caller allows it, and every such exit is listed
+in the session summary.
 """
 import sys
 
@@ -66,11 +68,14 @@ def _run_gpu(inp):
     return {k: v.numpy() for k, v in out.items()}
 
 
-def _compare_unit(inp, g, u, ures, qrows=None, check_O=True):
+def _compare_unit(inp, g, u, ures, qrows=None, check_O=True, allow_near_tie=False):
     w = inp["workload"]
     sel = ures.sel
-    matched = check_pivots(g["S"][u], int(g["r_eff"][u]), sel)
+    matched = check_pivots(g["S"][u], int(g["r_eff"][u]), sel, context=f"{w.name} unit {u}")
     full = matched == sel.r_eff
+    assert full or allow_near_tie, (
+        f"unit {u}: pivots diverge at a near tie at draw {matched}; the comparison of L, X and O "
+        f"would stop short")
     re = matched
     L = g["L"][u]
     scale = max(1.0, float(np.abs(sel.L).max()))
@@ -284,3 +289,33 @@ def test_many_units_mixed_early_stop():
         _compare_unit(inp, g, u, ref[u])
         stopped += int(g["r_eff"][u] < r)
     assert stopped >= 16
+
+
+def test_non_current_stream_with_concurrent_allocations():
+    """Every call gets stream= a stream that is not the current one.  While
+    its kernels run, the current stream allocates and overwrites blocks the
+    size of each workspace: memory the binding released to the current
+    stream's pool would be handed out and clobbered.  The outputs must equal
+    those of plain calls bit for bit."""
+    import torch
+    from nystr_rpcholesky_coreset_amd import wildcat as wc
+    w = I.scaled_workload(C4, q_heads=4, kv_heads=2, n=20000, m=64, r=512, seed=41)
+    inp = I.make_inputs(w)
+    ref = _run_gpu(inp)
+    Q, K, V = (to_device(inp[k], w.dtype) for k in "QKV")
+    u = torch.from_numpy(inp["u"]).cuda()
+    desc = wc.kv_desc(K, w.r, w.beta)
+    nsel, nw = wc.select_workspace_bytes(desc), wc.weights_workspace_bytes(desc)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    S, r_eff, L = wc.select(K, u, w.r, w.beta, stream=s)
+    junk = [torch.full((nsel,), 255, dtype=torch.uint8, device="cuda")]
+    K_S, X, vmin, vmax = wc.weights(K, V, S, r_eff, L, w.r, w.beta, stream=s)
+    junk.append(torch.full((nw,), 255, dtype=torch.uint8, device="cuda"))
+    O = wc.attend(Q, K_S, X, vmin, vmax, w.beta, stream=s)
+    junk.append(torch.full((O.numel() * 4,), 255, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    got = {"S": S, "r_eff": r_eff, "L": L, "X": X, "vmin": vmin, "vmax": vmax, "O": O}
+    for k, v in got.items():
+        np.testing.assert_array_equal(v.cpu().numpy(), ref[k], err_msg=k)
+    del junk

@@ -96,7 +96,8 @@ def test_streaming_paths_against_oracle(factor):
     Kd = I.to_f64(inp["K"], w.dtype)
     for unit in (0, 2):
         sel = orc.rpnys_select(Kd[unit, 0], inp["u"][unit], w.r, w.beta, w.tau, w.recentre, factor=factor)
-        k = check_pivots(S[unit], int(r_eff[unit]), sel, near=NEAR_TIE if factor == "f64" else NEAR_TIE_F32)
+        k = check_pivots(S[unit], int(r_eff[unit]), sel, near=NEAR_TIE if factor == "f64" else NEAR_TIE_F32,
+                         context=f"streamcheck {factor} unit {unit}")
         if k < sel.r_eff:
             print(f"unit {unit}: pivots match up to a near tie at draw {k}")
         tol = 1e-9 if factor == "f64" else 2e-6
