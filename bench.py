@@ -62,19 +62,18 @@ TRAFFIC_SUMMARY = {
 }
 
 
-def measured_traffic(w, factor="f64"):
-    """HBM bytes of one RPNys round measured with rocprofv3 FETCH_SIZE and
-    WRITE_SIZE (calibrated on a plain 1 GiB elementwise kernel), read from the
-    committed counter summary.  None unless that summary was taken on this
-    workload with the select kernel sources as they are now."""
+def read_pinned(path, w):
+    """Fields of a committed rocprofv3 summary's machine-readable block
+    (`key: value` lines), or None unless the summary was taken on workload w
+    with the kernel sources it names hashing as they are now."""
     import hashlib
     try:
         fields = {}
-        for line in open(TRAFFIC_SUMMARY[factor]):
+        for line in open(path):
             k, sep, v = line.strip().partition(": ")
             if sep:
                 fields[k] = v
-        if fields.get("workload") != w.name or fields.get("factor") != factor:
+        if fields.get("workload") != w.name:
             return None
         h = hashlib.sha256()
         for rel in fields["kernel_sources"].split():
@@ -82,15 +81,54 @@ def measured_traffic(w, factor="f64"):
                 h.update(f.read())
         if h.hexdigest() != fields["kernel_sources_sha256"]:
             return None
-        return float(fields["traffic_bytes_per_round"])
+        return fields
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic(w, factor="f64"):
+    """HBM bytes of one RPNys round measured with rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (calibrated on a plain 1 GiB elementwise kernel), read from the
+    committed counter summary.  None unless that summary was taken on this
+    workload with the select kernel sources as they are now."""
+    f = read_pinned(TRAFFIC_SUMMARY[factor], w)
+    if f is None or f.get("factor") != factor:
+        return None
+    try:
+        return float(f["traffic_bytes_per_round"])
+    except (KeyError, ValueError):
+        return None
+
+
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "contraction_mfma_kvcache_n32768_r1024.md")
+
+
+def mfma_evidence(w, bins):
+    """Matrix-core rate of the two exp-kernel contractions from the committed
+    rocprofv3 summary (kernel-trace durations and MFMA counters), only while
+    the contraction sources hash as they did when it was taken."""
+    if bins != 1:
+        return None
+    f = read_pinned(MFMA_SUMMARY, w)
+    if f is None:
+        return None
+    out = {"source": os.path.relpath(MFMA_SUMMARY, ROOT), "peak_tflops": MFMA_BF16_TFLOPS}
+    try:
+        for ph in ("weights", "attend"):
+            us, gflop = float(f[f"{ph}_trace_us"]), float(f[f"{ph}_gflop"])
+            out[ph] = {"kernel": f[f"{ph}_kernel"], "trace_us": us, "gflop": gflop,
+                       "tflops": gflop / us * 1e-3, "frac": gflop / us * 1e-3 / MFMA_BF16_TFLOPS,
+                       "mfma_busy_frac": float(f[f"{ph}_mfma_busy_frac"])}
+    except (KeyError, ValueError):
+        return None
+    return out
 
 
 def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
     """The oracle as it stands, timed on host cores on a bounded sample: whole
     kv units (select + weights + attend for their query heads), as many as fit
-    in about target_s seconds (at least one)."""
+    in about target_s seconds (at least one).  Returns the baseline object and
+    the oracle's results per unit: (unit, compress result, {q-head: O})."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -104,6 +142,7 @@ def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
     rows = 0
     t0 = time.perf_counter()
     units_done = 0
+    results = []
     for uidx in range(w.units):
         b, h = divmod(uidx, w.kv_heads)
         if bins == 1:
@@ -111,10 +150,12 @@ def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
         else:
             ur = orc.compress_unit_binned(K[b, h], V[b, h], inp["u"][uidx], w.r, bins, w.beta, w.tau, w.recentre,
                                           factor)
+        outs = {}
         for hq in range(h * group, (h + 1) * group):
             Q = I.to_f64(Qa[b, hq], w.dtype)
-            orc.plugin_attend(Q, ur.K_S, ur.X, ur.vmin, ur.vmax, w.beta)
+            outs[hq] = orc.plugin_attend(Q, ur.K_S, ur.X, ur.vmin, ur.vmax, w.beta)
             rows += Q.shape[0]
+        results.append((uidx, ur, outs))
         units_done += 1
         if time.perf_counter() - t0 > target_s:
             break
@@ -122,7 +163,34 @@ def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {"value": rows / dt, "unit": "query rows/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{units_done} of {w.units} kv units ({rows} query rows), full n={w.n}, r={w.r}; "
-                      f"{dt:.1f} s on {threads} BLAS threads (os.cpu_count()={os.cpu_count()})"}
+                      f"{dt:.1f} s on {threads} BLAS threads (os.cpu_count()={os.cpu_count()})"}, results
+
+
+def parity_vs_oracle(w, inp, bins, results, S_gpu, O_gpu):
+    """The timed path's last outputs against the oracle units of the CPU
+    baseline leg (same inputs and uniforms): pivots matched bit for bit (the
+    prefix up to the first difference, per unit or bin) and the largest
+    output error relative to max|V|."""
+    import numpy as np
+
+    from nystr_rpcholesky_coreset_amd import inputs as I
+    Vmax = float(np.abs(I.to_f64(inp["V"], w.dtype)).max())
+    matched = total = 0
+    err = 0.0
+    for uidx, ur, outs in results:
+        sels = [ur.sel] if bins == 1 else [p.sel for p in ur.bins]
+        for k, sel in enumerate(sels):
+            Sg = S_gpu[uidx * bins + k]
+            m = 0
+            while m < sel.r_eff and int(Sg[m]) == int(sel.S[m]):
+                m += 1
+            matched += m
+            total += sel.r_eff
+        b = uidx // w.kv_heads
+        for hq, Oo in outs.items():
+            err = max(err, float(np.abs(O_gpu[b, hq].astype(np.float64) - Oo).max()) / Vmax)
+    return {"units": len(results), "pivots_matched": matched, "pivots_total": total, "max_err_rel": err,
+            "tol": 2e-3 if w.dtype == "fp32" else 2e-2}
 
 
 def main():
@@ -191,7 +259,7 @@ def main():
         O = wc.attend(Q, K_S, X, vmin, vmax, w.beta)
         if ev:
             ev[3].record(stream)
-        return O, r_eff, (K_S, X, vmin, vmax)
+        return O, r_eff, (K_S, X, vmin, vmax), S
 
     for _ in range(args.warmup):
         step()
@@ -201,7 +269,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        O, r_eff, cache = step(evs[k])
+        O, r_eff, cache, S_last = step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ph = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(3)] for k in range(args.steps)])
@@ -315,6 +383,7 @@ def main():
         "attend_only_rows_per_s": rows / (t_att * 1e-3),
         "decode": decode,
         "exact_attention_gpu": exact,
+        "mfma": mfma_evidence(w, B),
         "roofline": {
             "kernel": "one RPNys round over all units" + (f" and their {B} bins" if B > 1 else "")
                       + ": rpc_step (factor/diagonal stream) + rpc_draw (next pivot) "
@@ -334,7 +403,9 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, B, factor=args.factor)
+        S_np, O_np = S_last.cpu().numpy(), O.cpu().numpy()
+        line["cpu_baseline"], results = cpu_baseline(w, inp, B, factor=args.factor)
+        line["parity"] = parity_vs_oracle(w, inp, B, results, S_np, O_np)
     print(json.dumps(line), flush=True)
 
 

@@ -277,8 +277,9 @@ wildcat_status wildcat_check_range(const wildcat_kv_desc* desc, const void* K,
                                    double* scratch, double* bounds,
                                    hipStream_t stream);
 
-/* Host.  Static description of a status code. */
-const char* wildcat_status_string(wildcat_status status);
+/* Host.  Static description of a status code (a wildcat_status value; any
+ * other int gives "unknown status"). */
+const char* wildcat_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -169,7 +169,7 @@ wildcat_status wildcat_merge_value_ranges(int32_t units, int32_t bins, int32_t d
   return e == hipSuccess ? WILDCAT_OK : WILDCAT_ERR_HIP;
 }
 
-const char* wildcat_status_string(wildcat_status status) {
+const char* wildcat_status_string(int status) {
   switch (status) {
     case WILDCAT_OK: return "ok";
     case WILDCAT_ERR_ARG: return "invalid argument (null or misaligned pointer, bad beta/tau/recentre/factor)";

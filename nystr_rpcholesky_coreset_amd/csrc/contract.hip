@@ -8,8 +8,8 @@
 // range), CompressKV / Alg. 2 and WtdAttn / Alg. 3 paragraphs.]
 //
 // bf16 inputs with d >= 32 run expmm32 (32x32x16 MFMA, described at the
-// kernel); d = 16 runs expmm_bf16, and fp32 inputs run expmm_f32 on the vector
-// ALU.  expmm_bf16: a workgroup of NW waves owns 16 rows of the
+// kernel); d = 16 runs expmm_bf16, and fp32 inputs run expmm_f32m on the
+// fp32 matrix cores (described at the kernel).  expmm_bf16: a workgroup of NW waves owns 16 rows of the
 // left operand per wave (fragments kept in registers) and streams the right
 // operand in tiles of 64 rows through LDS.  Per 32 right rows a wave issues
 //   scores^T (16 rows x 16 cols) x2 : v_mfma_f32_16x16x32_bf16 over d
@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "ordered.hpp"
 #include "weights_layout.hpp"
 
 namespace wc {
@@ -670,111 +671,177 @@ __global__ __launch_bounds__(64 * NWAVE) void expmm32(ContractArgs p) {
   }
 }
 
-// fp32 inputs: the same contraction on the vector ALU in fp32 (P is not
-// rounded).  A workgroup owns 64 left rows; thread (row, quarter) accumulates
-// every fourth output column of its row.
-template <int D, int MODE>
-__global__ __launch_bounds__(kBlock) void expmm_f32(ContractArgs p) {
-  __shared__ float sB[kTileKeys][D + 1];
-  __shared__ float sV[kTileKeys][D + 1];
-  __shared__ float sE[kTileKeys];
-  __shared__ float sC[kTileKeys];
-  const int t = threadIdx.x, rl = t >> 2, qc = t & 3;
+// fp32 inputs: the same contraction on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32, fp32 products and sums; P stays fp32).  A
+// workgroup of NW waves owns 16 left rows per wave (their fragments in
+// registers) and streams the right operand through LDS in tiles of KT rows.
+// Per 16 right rows a wave issues
+//   scores^T (16 right x 16 left) : D/4 MFMAs over d  -> lane (r16, g) holds
+//                                   the scores of left row r16 with right
+//                                   rows 4g .. 4g + 3
+//   P = exp2(...) in fp32, masked
+//   P x [V] (16 left x 16 cols)   : 4 MFMAs per 16 columns, MFMA v taking
+//                                   right rows {4g + v}: P never leaves the
+//                                   registers
+// and the last column ([.., 1] or w) on the vector ALU.  LDS rows have a
+// pitch of D + 4 floats, which keeps both the score and the value reads
+// free of bank conflicts.  Output rows of the 16x16x4 MFMA: element v of
+// lane (r16, g) is row 4g + v, column r16.
+template <int D, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) void expmm_f32m(ContractArgs p) {
+  constexpr int NTH = 64 * NW;
+  constexpr int KT = 64;             // right rows per LDS tile
+  constexpr int KP = D + 4;          // LDS pitch (floats)
+  constexpr int DC = D / 4;          // score MFMAs per 16 right rows
+  constexpr int CT = D / 16;         // value column tiles
+  __shared__ __attribute__((aligned(16))) float sB[KT * KP];
+  __shared__ __attribute__((aligned(16))) float sV[KT * KP];
+  __shared__ float sE[KT];           // attend: w; weights: 1 on valid rows
+  __shared__ float sC[KT];           // weights: per-key offsets * log2(e)
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
   const int unit = blockIdx.z, unitB = unit / p.group;
-  const int a0 = blockIdx.y * kTileRows, split = blockIdx.x;
+  const int a0 = blockIdx.y * 16 * NW;
+  const int split = blockIdx.x;
   const int b_begin = MODE == kModeWeights ? split * p.chunk : 0;
   int b_end = MODE == kModeWeights ? min(p.rowsB, b_begin + p.chunk) : p.rowsB;
-  if (MODE == kModeAttend && p.causal) b_end = min(b_end, p.causal_from + a0 + kTileRows);
+  if (MODE == kModeAttend && p.causal) b_end = min(b_end, p.causal_from + a0 + 16 * NW);
+
   const float* A = reinterpret_cast<const float*>(p.A) + (size_t)unit * p.rowsA * D;
   const float* B = reinterpret_cast<const float*>(p.B) + (size_t)unitB * p.rowsB * D;
-  const int row = a0 + rl;
-  float arow[D];
+  // left-row fragments (B operand of the score MFMA): row a0 + 16 wave + r16, d = 4 dc + g
+  const int arow = a0 + wave * 16 + r16;
+  float afrag[DC];
 #pragma unroll
-  for (int c = 0; c < D; ++c) arow[c] = row < p.rowsA ? A[(size_t)row * D + c] : 0.0f;
-  const float rc = (MODE == kModeWeights && p.rowc != nullptr && row < p.rowsA) ? p.rowc[(size_t)unit * p.rowsA + row] : 0.0f;
-  constexpr int NC = (D + 4) / 4;   // columns 0..D (D+1 of them), strided by 4
-  float acc[NC];
+  for (int dc = 0; dc < DC; ++dc) afrag[dc] = arow < p.rowsA ? A[(size_t)arow * D + 4 * dc + g] : 0.0f;
+  float rc2 = 0.0f;
+  if (MODE == kModeWeights && p.rowc != nullptr && arow < p.rowsA) rc2 = p.rowc[(size_t)unit * p.rowsA + arow] * kLog2e;
+  const float sc2 = p.scale * kLog2e;
+
+  f32x4 oacc[CT];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) acc[j] = 0.0f;
-  for (int b0 = b_begin; b0 < b_end; b0 += kTileKeys) {
-    for (int q = t; q < kTileKeys * D; q += kBlock) {
-      const int rr = q / D, c = q % D, b = b0 + rr;
-      sB[rr][c] = b < b_end ? B[(size_t)b * D + c] : 0.0f;
-      float v = 0.0f;
+  for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float eacc = 0.0f;
+
+  for (int b0 = b_begin; b0 < b_end; b0 += KT) {
+    // ---- stage the right tile and its values (zeros past b_end)
+    for (int q = t; q < KT * (D / 4); q += NTH) {
+      const int row = q / (D / 4), c4 = q % (D / 4);
+      const int b = b0 + row;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (b < b_end) {
-        v = MODE == kModeWeights ? reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * D + c]
-                                 : reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * (D + 1) + c];
+        kv = *reinterpret_cast<const float4*>(B + (size_t)b * D + 4 * c4);
+        if (MODE == kModeWeights) {
+          vv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.Vs) +
+                                                ((size_t)unitB * p.rowsB + b) * D + 4 * c4);
+        } else {
+          const float* X = reinterpret_cast<const float*>(p.Vs) + ((size_t)unitB * p.rowsB + b) * (D + 1) + 4 * c4;
+          vv = make_float4(X[0], X[1], X[2], X[3]);
+        }
       }
-      sV[rr][c] = v;
+      *reinterpret_cast<float4*>(&sB[row * KP + 4 * c4]) = kv;
+      *reinterpret_cast<float4*>(&sV[row * KP + 4 * c4]) = vv;
     }
-    if (t < kTileKeys) {
-      const int b = b0 + t;
-      if (MODE == kModeWeights) {
-        sV[t][D] = b < b_end ? 1.0f : 0.0f;
-        sC[t] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] : 0.0f;
+    for (int q = t; q < KT; q += NTH) {
+      const int b = b0 + q;
+      if (MODE == kModeAttend) {
+        sE[q] = b < b_end ? reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * (D + 1) + D] : 0.0f;
       } else {
-        sV[t][D] = b < b_end ? reinterpret_cast<const float*>(p.Vs)[((size_t)unitB * p.rowsB + b) * (D + 1) + D] : 0.0f;
-        sC[t] = 0.0f;
+        sE[q] = b < b_end ? 1.0f : 0.0f;
+        sC[q] = (p.colc != nullptr && b < b_end) ? p.colc[(size_t)unitB * p.rowsB + b] * kLog2e : 0.0f;
       }
-      sE[t] = b < b_end ? 1.0f : 0.0f;
     }
     __syncthreads();
-    for (int k = 0; k < kTileKeys; ++k) {
-      float s = 0.0f;
+
 #pragma unroll
-      for (int c = 0; c < D; ++c) s = fmaf(arow[c], sB[k][c], s);
-      const float pk = (sE[k] != 0.0f && (MODE != kModeAttend || visible(p, b0 + k, row)))
-                           ? expf(fmaf(s, p.scale, rc + sC[k])) : 0.0f;
+    for (int kb = 0; kb < KT / 16; ++kb) {
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = qc + 4 * j;
-        if (c <= D) acc[j] = fmaf(pk, sV[k][c], acc[j]);
+      for (int dc = 0; dc < DC; ++dc)
+        s4 = __builtin_amdgcn_mfma_f32_16x16x4f32(sB[(16 * kb + r16) * KP + 4 * dc + g], afrag[dc], s4, 0, 0, 0);
+      // s4[v] = score of left row r16 with right row 16 kb + 4 g + v
+      float pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kk = 16 * kb + 4 * g + v;
+        float arg = fmaf(s4[v], sc2, rc2);
+        if (MODE == kModeWeights) arg += sC[kk];
+        const bool keep = MODE == kModeWeights ? sE[kk] != 0.0f
+                                               : (b0 + kk < b_end && visible(p, b0 + kk, arow));
+        pv[v] = keep ? exp2f(arg) : 0.0f;
+        eacc = fmaf(pv[v], sE[kk], eacc);
       }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[v], sV[(16 * kb + 4 * g + v) * KP + 16 * ct + r16],
+                                                          oacc[ct], 0, 0, 0);
     }
     __syncthreads();
   }
+
+  // eacc: partial over this lane's right rows -> full sum for left row r16.
+  eacc += __shfl_xor(eacc, 16, 64);
+  eacc += __shfl_xor(eacc, 32, 64);
+
+  // oacc[ct][v] = result for left row 16 wave + 4 g + v, column 16 ct + r16.
   if (MODE == kModeWeights) {
-    if (row < p.rowsA) {
-      float* Y = p.out + (((size_t)split * p.units + unit) * p.rowsA + row) * (D + 1);
+    float* Y = p.out + ((size_t)split * p.units + unit) * p.rowsA * (D + 1);
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = qc + 4 * j;
-        if (c <= D) Y[c] = acc[j];
+    for (int v = 0; v < 4; ++v) {
+      const int row = a0 + wave * 16 + 4 * g + v;
+      if (row < p.rowsA) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[(size_t)row * (D + 1) + 16 * ct + r16] = oacc[ct][v];
       }
     }
+    if (g == 0 && arow < p.rowsA) Y[(size_t)arow * (D + 1) + D] = eacc;
   } else {
-    // the normaliser (column D) sits in the thread with qc == D % 4
-    __shared__ float sN[kTileRows];
-    if (qc == (D & 3)) sN[rl] = acc[D / 4];
-    __syncthreads();
-    if (row < p.rowsA) {
-      const float e = sN[rl];
-      float* O = p.out + ((size_t)unit * p.rowsA + row) * D;
-      float lo[NC], hi[NC];   // read before any store: O stores could alias them
-      const size_t rbase = p.range_rows ? ((size_t)unitB * p.rowsA + row) * D : (size_t)unitB * D;
+    float* O = p.out + (size_t)unit * p.rowsA * D;
+    float lo[CT], hi[CT];   // read before any store: O stores could alias them
+    if (!p.range_rows) {
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = qc + 4 * j;
-        lo[j] = c < D ? p.vmin[rbase + c] : 0.0f;
-        hi[j] = c < D ? p.vmax[rbase + c] : 0.0f;
+      for (int ct = 0; ct < CT; ++ct) {
+        lo[ct] = p.vmin[(size_t)unitB * D + 16 * ct + r16];
+        hi[ct] = p.vmax[(size_t)unitB * D + 16 * ct + r16];
       }
+    }
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int c = qc + 4 * j;
-        if (c < D) O[c] = fminf(fmaxf(acc[j] / e, lo[j]), hi[j]);
+    for (int v = 0; v < 4; ++v) {
+      const int rl = 4 * g + v;
+      const float e = __shfl(eacc, rl, 64);
+      const int row = a0 + wave * 16 + rl;
+      if (row < p.rowsA) {
+        if (p.range_rows) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const size_t k = ((size_t)unitB * p.rowsA + row) * D + 16 * ct + r16;
+            lo[ct] = p.vmin[k];
+            hi[ct] = p.vmax[k];
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          O[(size_t)row * D + 16 * ct + r16] = fminf(fmaxf(oacc[ct][v] / e, lo[ct]), hi[ct]);
       }
     }
   }
 }
 
 // K_S[u][j] = K[u][S[u][j]] for j < r_eff, zero rows after; optional per-pivot
-// exponent offsets for recentring: rowc = c (|kbar|^2 - <k_s, kbar>).
+// exponent offsets for recentring: rowc = c (|kbar|^2 - <k_s, kbar>).  Also
+// initialises the value-range slots that value_range_part reduces into.
 template <typename TK, int D>
 __global__ __launch_bounds__(kBlock) void gather_pivots(const TK* K, const int32_t* S, const int32_t* r_eff,
                                                         TK* K_S, const double* kbar, float* rowc,
-                                                        int n, int r, double c) {
+                                                        int n, int r, double c, int* mmslot) {
   __shared__ double red[kBlock];
   const int u = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  // the value-range slots of unit u start at the identities of min / max
+  if (j == 0)
+    for (int e = t; e < 2 * D; e += kBlock) mmslot[(size_t)u * 2 * D + e] = e < D ? 0x7FFFFFFF : (int)0x80000000;
   const bool live = j < r_eff[u];
   const int s = live ? S[(size_t)u * r + j] : 0;
   for (int e = t; e < D; e += kBlock) {
@@ -829,37 +896,54 @@ __global__ __launch_bounds__(kBlock) void key_mean(const TK* K, double* kbar, in
   }
 }
 
-// Column min / max of V: partials over kMinMaxRows rows, then a reduction.
-// Each thread reads 16-byte groups of one row; 256 threads cover
-// 256 / (D / G) rows per pass, G = elements per 16 bytes.
+// Column min / max of V.  Workgroup (blk, u) covers rows [blk R, blk R + R),
+// R = kMinMaxRows: thread t reads the 16-byte group t % NG of rows t / NG + RP p
+// (RP = 256 / NG rows per pass), UNR loads issued before their min / max;
+// rows past n re-read row n-1 (harmless for a min / max).  The RP row phases
+// meet in LDS, then one integer atomic min / max per column on the
+// order-encoded value (slots initialised by gather_pivots, decoded by the
+// solve's first launch).
 template <typename TK, int D>
-__global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, float* part, int n, int nmm) {
-  constexpr int G = 16 / sizeof(TK);
+__global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, int* slot, int n) {
+  constexpr int G = 16 / sizeof(TK);   // elements per 16 bytes
   constexpr int NG = D / G;            // groups per row
   constexpr int RP = kBlock / NG;      // rows per pass
+  constexpr int NPASS = kMinMaxRows / RP;
+  constexpr int UNR = NPASS < 8 ? NPASS : 8;
+  static_assert(NPASS % UNR == 0, "passes");
   __shared__ float smn[RP][D + 1], smx[RP][D + 1];
   const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
   const int grp = t % NG, ph = t / NG;
-  const int l0 = blk * kMinMaxRows, l1 = min(n, l0 + kMinMaxRows);
+  const int l0 = blk * kMinMaxRows;
+  const TK* Vu = V + (size_t)u * n * D + grp * G;
   float mn[G], mx[G];
 #pragma unroll
   for (int q = 0; q < G; ++q) { mn[q] = INFINITY; mx[q] = -INFINITY; }
-  for (int l = l0 + ph; l < l1; l += RP) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(V + ((size_t)u * n + l) * D + grp * G);
-    float x[G];
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    if constexpr (G == 8) {
+#pragma unroll 1
+  for (int p0 = 0; p0 < NPASS; p0 += UNR) {
+    uint4 raw[UNR];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[2 * q] = __uint_as_float(w[q] << 16);
-        x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+    for (int j = 0; j < UNR; ++j) {
+      const int l = min(l0 + ph + RP * (p0 + j), n - 1);
+      raw[j] = *reinterpret_cast<const uint4*>(Vu + (size_t)l * D);
     }
 #pragma unroll
-    for (int q = 0; q < G; ++q) { mn[q] = fminf(mn[q], x[q]); mx[q] = fmaxf(mx[q], x[q]); }
+    for (int j = 0; j < UNR; ++j) {
+      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      float x[G];
+      if constexpr (G == 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          x[2 * q] = __uint_as_float(w[q] << 16);
+          x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < G; ++q) { mn[q] = fminf(mn[q], x[q]); mx[q] = fmaxf(mx[q], x[q]); }
+    }
   }
 #pragma unroll
   for (int q = 0; q < G; ++q) { smn[ph][grp * G + q] = mn[q]; smx[ph][grp * G + q] = mx[q]; }
@@ -867,24 +951,9 @@ __global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, float* p
   for (int c = t; c < D; c += kBlock) {
     float a = INFINITY, b = -INFINITY;
     for (int p = 0; p < RP; ++p) { a = fminf(a, smn[p][c]); b = fmaxf(b, smx[p][c]); }
-    float* o = part + (((size_t)u * nmm + blk) * 2) * D;
-    o[c] = a;
-    o[D + c] = b;
+    atomicMin(&slot[((size_t)u * 2) * D + c], ord_enc(a));
+    atomicMax(&slot[((size_t)u * 2 + 1) * D + c], ord_enc(b));
   }
-}
-
-__global__ __launch_bounds__(kBlock) void value_range_final(const float* part, float* vmin, float* vmax, int d, int nmm, int U) {
-  const int e = blockIdx.x * kBlock + threadIdx.x;
-  if (e >= U * d) return;
-  const int u = e / d, c = e % d;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int b = 0; b < nmm; ++b) {
-    const float* o = part + (((size_t)u * nmm + b) * 2) * d;
-    mn = fminf(mn, o[c]);
-    mx = fmaxf(mx, o[d + c]);
-  }
-  vmin[e] = mn;
-  vmax[e] = mx;
 }
 
 // Binned RPNys: the value range of a unit is the min / max over its bins'
@@ -927,7 +996,7 @@ inline int attend_key_split(int Uq, int m, int r, int d, bool bf16) {
 // bf16 with d >= 32 runs the 32x32x16 kernel with 2, 4 or 8 waves (32 left
 // rows each, see mfma32_waves), or for attend with few query rows the
 // 8-wave key-split form (attend_key_split); bf16 d = 16 the 16x16x32 kernel;
-// fp32 the vector-ALU kernel.  contract_rows_per_wg gives the same tiling to
+// fp32 the 16x16x4 fp32 kernel.  contract_rows_per_wg gives the same tiling to
 // the workspace layout.
 template <int D, int MODE>
 static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream_t st) {
@@ -961,7 +1030,7 @@ static void launch_expmm(bool bf16, const ContractArgs& a, int nsplit, hipStream
       expmm_bf16<D, MODE, 4><<<grid, 256, 0, st>>>(a);
     }
   } else {
-    expmm_f32<D, MODE><<<grid, kBlock, 0, st>>>(a);
+    expmm_f32m<D, MODE, 4><<<grid, 256, 0, st>>>(a);
   }
 }
 
@@ -989,11 +1058,10 @@ static void launch_weights_prep(int U, int n, int r, double c, int recentre, con
     key_mean<TK, D><<<U, kBlock, 0, st>>>(Kt, kbar, n);
     key_offsets<TK, D><<<dim3((n + kBlock - 1) / kBlock, U), kBlock, 0, st>>>(Kt, kbar, colc, n, c);
   }
+  int* mm = reinterpret_cast<int*>(w + lay.mmslot);
   gather_pivots<TK, D><<<dim3(r, U), kBlock, 0, st>>>(Kt, S, r_eff, reinterpret_cast<TK*>(K_S), kbar,
-                                                       recentre ? rowc : nullptr, n, r, c);
-  float* mm = reinterpret_cast<float*>(w + lay.mmpart);
-  value_range_part<TK, D><<<dim3(lay.nmm, U), kBlock, 0, st>>>(reinterpret_cast<const TK*>(V), mm, n, lay.nmm);
-  value_range_final<<<(U * D + kBlock - 1) / kBlock, kBlock, 0, st>>>(mm, vmin, vmax, D, lay.nmm, U);
+                                                       recentre ? rowc : nullptr, n, r, c, mm);
+  value_range_part<TK, D><<<dim3(lay.nmm, U), kBlock, 0, st>>>(reinterpret_cast<const TK*>(V), mm, n);
 }
 
 template <typename TK>
@@ -1010,8 +1078,8 @@ static hipError_t launch_prep_d(int d, int U, int n, int r, double c, int recent
   return hipGetLastError();
 }
 
-hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, double* LT,
-                       double* Dinv, const int32_t* r_eff, float* X, hipStream_t st);
+hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, const double* L, const int32_t* r_eff,
+                       float* X, float* vmin, float* vmax, const WeightsLayout& lay, char* ws, hipStream_t st);
 
 // CompressKV after selection: K_S, value range, Y = h_tau(K_S, K) [V, 1], X.
 hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int recentre, const void* K,
@@ -1031,8 +1099,7 @@ hipError_t launch_weights(int bf16, int U, int n, int d, int r, double c, int re
   a.scale = (float)c;
   e = launch_expmm_d<kModeWeights>(bf16 != 0, d, a, lay.sp.nsplit, st);
   if (e != hipSuccess) return e;
-  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, reinterpret_cast<double*>(w + lay.LT),
-                     reinterpret_cast<double*>(w + lay.Dinv), r_eff, X, st);
+  return launch_trsm(U, r, d, a.out, lay.sp.nsplit, L, r_eff, X, vmin, vmax, lay, w, st);
 }
 
 // WtdAttn: O = clip(h(Q, K_S) X / (h(Q, K_S) w)).

@@ -37,29 +37,52 @@ struct ContractSplit {
   }
 };
 
+// Geometry of the triangular solves: diagonal blocks of b rows (the rank
+// padded to rp, a multiple of b), and the d+1 right-hand-side columns padded
+// to cp = 16 nct, taken nc column tiles of 16 at a time.
+#ifndef WILDCAT_SOLVE_BMAX
+#define WILDCAT_SOLVE_BMAX 512   // largest diagonal block of the solves (a power of 2, >= 64)
+#endif
+struct SolveGeom {
+  int b, rp, nct, cp, nc;
+  SolveGeom(int r, int d) {
+    b = 64;
+    while (b < r && b < WILDCAT_SOLVE_BMAX) b *= 2;
+    rp = (r + b - 1) / b * b;
+    nct = (d + 1 + 15) / 16;      // 2, 3, 5, 9 for d = 16, 32, 64, 128
+    cp = 16 * nct;
+    nc = nct == 9 ? 3 : nct;
+  }
+};
+
 // Weights workspace:
 //   ypart   [nsplit][U][r][d+1] fp32   split-n partial contractions
-//   mmpart  [U][nmm][2][d]      fp32   partial column min / max of V
+//   mmslot  [U][2][d]           int32  column min / max of V, order-encoded (atomics)
 //   kbar    [U][d]              fp64   key mean (recentring only)
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
-//   LT      [U][r][r]           fp64   transposed pivot block for the forward solve
-//   Dinv    [U][r/64+1][64][64] fp64   inverses of the 64x64 diagonal blocks of the pivot block
-constexpr int kMinMaxRows = 1024;   // rows of V per min/max partial
+//   band    [U][rp][b]          fp64   inverses of the b x b diagonal blocks of the pivot block
+//   t1      [U][rp/2][b/2]      fp64   products of the block-inverse doubling
+//   yw, zw  [U][rp][cp]         fp64   right-hand sides during the two sweeps (yw ends as X)
+constexpr int kMinMaxRows = 512;    // rows of V per value-range workgroup
 struct WeightsLayout {
   ContractSplit sp;
-  int nmm;
-  size_t ypart, mmpart, kbar, rowc, colc, LT, Dinv, total;
-  WeightsLayout(int U, int n, int d, int r, bool bf16) : sp(U, r, n, contract_rows_per_wg(d, r, bf16)) {
+  SolveGeom sg;
+  int nmm;                          // value-range workgroups per unit
+  size_t ypart, mmslot, kbar, rowc, colc, band, t1, yw, zw, total;
+  WeightsLayout(int U, int n, int d, int r, bool bf16)
+      : sp(U, r, n, contract_rows_per_wg(d, r, bf16)), sg(r, d) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
     size_t o = 0;
     ypart = o;  o += al256((size_t)sp.nsplit * U * r * (d + 1) * 4);
-    mmpart = o; o += al256((size_t)U * nmm * 2 * d * 4);
+    mmslot = o; o += al256((size_t)U * 2 * d * 4);
     kbar = o;   o += al256((size_t)U * d * 8);
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
-    LT = o;     o += al256((size_t)U * r * r * 8);
-    Dinv = o;   o += al256((size_t)U * (r / 64 + 1) * 64 * 64 * 8);
+    band = o;   o += al256((size_t)U * sg.rp * sg.b * 8);
+    t1 = o;     o += al256((size_t)U * (sg.rp / 2) * (sg.b / 2) * 8);
+    yw = o;     o += al256((size_t)U * sg.rp * sg.cp * 8);
+    zw = o;     o += al256((size_t)U * sg.rp * sg.cp * 8);
     total = o;
   }
 };
