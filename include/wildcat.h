@@ -68,7 +68,8 @@ typedef enum {
   WILDCAT_ERR_SHAPE = -3,      /* sizes out of range (see the descriptors) */
   WILDCAT_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required */
   WILDCAT_ERR_RANGE = -5,      /* wildcat_check_range: an exponent bound exceeds WILDCAT_RANGE_LIMIT */
-  WILDCAT_ERR_HIP = -6         /* a kernel launch or a copy failed */
+  WILDCAT_ERR_HIP = -6,        /* a kernel launch or a copy failed */
+  WILDCAT_ERR_SCRATCH = -7     /* wildcat_decode_noalloc: the call needs more than its static scratch */
 } wildcat_status;
 
 /* Largest exponent argument wildcat_check_range accepts.  exp(64) leaves a
@@ -222,6 +223,31 @@ wildcat_status wildcat_decode(const wildcat_q_desc* desc, const void* Q,
                               const void* K_new, const void* V_new, float* O,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * Generation over the compressed cache with no allocation, for callers that
+ * cannot allocate device memory or pass a workspace (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and kernels as wildcat_decode, whose workspace is here a
+ * static device array of WILDCAT_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU it runs on, held until the process ends; its device address
+ * is looked up on the first call on each device).  It calls no allocator.
+ * Returns WILDCAT_ERR_SCRATCH, before any launch, when
+ * wildcat_decode_workspace_bytes(desc) exceeds that size (e.g. 32 query
+ * heads over 8 kv heads, d = 128, r = 1024: up to 1,878 new tokens per call;
+ * one new token needs 130 KB), and the status codes of wildcat_decode
+ * otherwise (an invalid descriptor: WILDCAT_ERR_ARG or WILDCAT_ERR_SHAPE).
+ * Every call on one GPU uses the same scratch: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  Nothing carries over between calls (every scratch byte read is
+ * written first in the same call).
+ */
+#define WILDCAT_NOALLOC_SCRATCH_BYTES (32u << 20)
+wildcat_status wildcat_decode_noalloc(const wildcat_q_desc* desc, const void* Q,
+                                      const void* K_S, const float* X,
+                                      const float* vmin, const float* vmax,
+                                      const void* K_new, const void* V_new, float* O,
+                                      hipStream_t stream);
 
 /*
  * Binned RPNys  [WildCat, RPNys / Alg. 1 paragraph: the divide-and-conquer

@@ -28,7 +28,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwildcat.so")
 STREAMCHECK_LIB = os.path.join(HERE, "libwildcat_streamcheck.so")
 STREAMCHECK_DEFINES = ["-DWILDCAT_SELECT_CACHED_BYTES=0", "-DWILDCAT_SELECT_KEEP_BYTES=(2ull<<20)"]
-SOURCES = ["api.hip", "select.hip", "contract.hip", "trsm.hip", "guard.hip"]
+SOURCES = ["api.hip", "select.hip", "contract.hip", "trsm.hip", "guard.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HOSTSAN_LIB = os.path.join(HERE, "libwildcat_hostsan.so")

@@ -178,6 +178,7 @@ const char* wildcat_status_string(int status) {
     case WILDCAT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case WILDCAT_ERR_RANGE: return "an exponent bound of the inputs exceeds WILDCAT_RANGE_LIMIT (or is not finite)";
     case WILDCAT_ERR_HIP: return "HIP launch failed";
+    case WILDCAT_ERR_SCRATCH: return "the call needs more than the static scratch of the no-allocation entry point";
   }
   return "unknown status";
 }

@@ -36,14 +36,16 @@ WILDCAT_ERR_SHAPE = -3
 WILDCAT_ERR_WORKSPACE = -4
 WILDCAT_ERR_RANGE = -5
 WILDCAT_ERR_HIP = -6
+WILDCAT_ERR_SCRATCH = -7
 RANGE_LIMIT = 64.0    # WILDCAT_RANGE_LIMIT
+NOALLOC_SCRATCH_BYTES = 32 << 20   # WILDCAT_NOALLOC_SCRATCH_BYTES
 WILDCAT_FP32 = 0
 WILDCAT_BF16 = 1
 
 EXPORTED = (
     "wildcat_select_workspace_bytes", "wildcat_weights_workspace_bytes", "wildcat_select",
     "wildcat_weights", "wildcat_attend", "wildcat_decode_workspace_bytes", "wildcat_decode",
-    "wildcat_merge_value_ranges", "wildcat_check_range", "wildcat_status_string",
+    "wildcat_merge_value_ranges", "wildcat_check_range", "wildcat_status_string", "wildcat_decode_noalloc",
 )
 
 
@@ -83,6 +85,8 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.wildcat_decode.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                    _vp]
     lib.wildcat_decode.restype = ctypes.c_int
+    lib.wildcat_decode_noalloc.argtypes = [ctypes.POINTER(QDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.wildcat_decode_noalloc.restype = ctypes.c_int
     lib.wildcat_merge_value_ranges.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
     lib.wildcat_merge_value_ranges.restype = ctypes.c_int
     lib.wildcat_check_range.argtypes = [ctypes.POINTER(KVDesc), _vp, ctypes.POINTER(QDesc), _vp, _vp,
@@ -222,6 +226,18 @@ def decode(Q, K_S, X, vmin, vmax, K_new, V_new, beta, workspace=None, stream=Non
                                   _ptr(K_new), _ptr(V_new), _ptr(O), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)), "wildcat_decode")
     return O
+
+
+def decode_noalloc(Q, K_S, X, vmin, vmax, K_new, V_new, beta, out, stream=None):
+    """wildcat_decode_noalloc: wildcat_decode with the library's static
+    scratch instead of a workspace; `out` (O) must be given, nothing is
+    allocated.  Calls overlapping on one GPU race on that scratch."""
+    B, Hq, m, d = Q.shape
+    Hkv, r = K_S.shape[1], K_S.shape[2]
+    desc = QDesc(B, Hq, Hkv, m, d, r, float(beta), _dtype_code(Q))
+    _check(lib.wildcat_decode_noalloc(ctypes.byref(desc), _ptr(Q), _ptr(K_S), _ptr(X), _ptr(vmin), _ptr(vmax),
+                                      _ptr(K_new), _ptr(V_new), _ptr(out), _stream(stream)), "wildcat_decode_noalloc")
+    return out
 
 
 def check_range(K, r, beta, tau=1.0, recentre=False, Q=None, scratch=None, stream=None):

@@ -153,7 +153,7 @@ def test_check_range_rejects_bad_pointers():
 
 def test_status_strings():
     for st in (wc.WILDCAT_OK, wc.WILDCAT_ERR_ARG, wc.WILDCAT_ERR_DTYPE, wc.WILDCAT_ERR_SHAPE,
-               wc.WILDCAT_ERR_WORKSPACE, wc.WILDCAT_ERR_RANGE, wc.WILDCAT_ERR_HIP):
+               wc.WILDCAT_ERR_WORKSPACE, wc.WILDCAT_ERR_RANGE, wc.WILDCAT_ERR_HIP, wc.WILDCAT_ERR_SCRATCH):
         assert wc.lib.wildcat_status_string(st) and b"unknown" not in wc.lib.wildcat_status_string(st)
     assert b"unknown" in wc.lib.wildcat_status_string(42)
 
@@ -213,3 +213,17 @@ def test_float32_factor_halves_the_factor_workspace():
     assert a - b >= U * r * npad * 4 - 512
     assert b > U * r * npad * 4
     assert wc.weights_workspace_bytes(_kv(factor=1)) == wc.weights_workspace_bytes(_kv(factor=0))
+
+
+def test_decode_noalloc_validation_before_any_launch():
+    """wildcat_decode_noalloc rejects an invalid descriptor and a call larger
+    than its static scratch on the host, before touching the GPU."""
+    q = wc.QDesc(1, 32, 8, 1879, 128, 1024, 0.1, wc.WILDCAT_BF16)
+    assert wc.decode_workspace_bytes(q) > wc.NOALLOC_SCRATCH_BYTES
+    call = wc.lib.wildcat_decode_noalloc
+    assert call(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SCRATCH
+    q.m = 1878
+    assert wc.decode_workspace_bytes(q) <= wc.NOALLOC_SCRATCH_BYTES
+    q.d = 100
+    assert call(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_SHAPE
+    assert call(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == wc.WILDCAT_ERR_ARG
