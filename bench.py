@@ -4,13 +4,16 @@ One step = wildcat_select + wildcat_weights + wildcat_attend over the whole
 synthetic workload (inputs already resident in HBM).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--bins B] [--no-cpu-baseline] [--copy-calibration]
+                    [--bins B] [--factor f64|f32] [--recentre] [--no-cpu-baseline]
+                    [--copy-calibration]
 
 Default workload: KV-cache compression with GQA, 32 query heads over 8 kv
 heads, n = 32768 keys, d = 128, r = 1024 pivots per kv head, 64 queries per
 query head, bf16 inputs.  --bins B > 1 times the binned variant (B contiguous
 key bins per kv head, r/B pivots and block-diagonal Nystroem weights per bin);
-the default B = 1 is plain RPNys.
+the default B = 1 is plain RPNys.  --recentre runs select and weights on the
+keys minus their per-unit mean (the pages' CompressKV recentring), with the
+same inputs and uniforms.
 """
 from __future__ import annotations
 
@@ -202,6 +205,8 @@ def main():
     ap.add_argument("--bins", type=int, default=1, help="key bins per kv head (1: plain RPNys)")
     ap.add_argument("--factor", choices=("f64", "f32"), default="f64",
                     help="storage of the RPNys factor (f32: the faster selection; all arithmetic stays fp64)")
+    ap.add_argument("--recentre", action="store_true",
+                    help="select and weights on the keys minus their per-unit mean")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain elementwise kernel over 1 GiB (1 GiB read + 1 GiB write), "
@@ -220,6 +225,8 @@ def main():
     from nystr_rpcholesky_coreset_amd import wildcat as wc
 
     w = I.WORKLOADS[args.workload]
+    if args.recentre:
+        w = I.scaled_workload(w, recentre=True)   # same inputs and uniforms (same seed)
     e = 2 if w.dtype == "bf16" else 4
     inp = I.make_inputs(w, new_tokens=True)
     dev = torch.device("cuda:0")
@@ -372,10 +379,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64+bf16" if w.dtype == "bf16" else "f64+fp32",
-        "data": f"synthetic (seeded '{w.recipe}' recipe with the shapes of the {w.name} workload)",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+        "data": f"synthetic (seeded '{w.recipe}' recipe with the shapes of the {args.workload} workload)",
+        "config": {"workload": args.workload, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "n": w.n, "m": w.m, "d": w.d, "r": w.r, "bins": B, "beta": w.beta, "input_dtype": w.dtype,
-                   "factor": args.factor},
+                   "factor": args.factor, "recentre": bool(w.recentre)},
         "phases_ms": {"select": t_sel, "weights": t_wts, "attend": t_att},
         "rpcholesky_ms": t_sel,
         "select_hbm_frac": sb / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -26,13 +26,16 @@
  *    b * kv_heads + h / (q_heads / kv_heads) (contiguous GQA groups).
  *  - The caller allocates and owns every buffer, including the workspace
  *    whose size the *_workspace_bytes queries return.  The library allocates
- *    no device memory.  Its only state is, per device, a few auxiliary
- *    default-priority streams and events that wildcat_select creates on its
- *    first call and keeps until the process ends: it splits the units into
- *    groups, forks the groups onto those streams with an event recorded on
- *    `stream`, and joins them back into `stream` before it returns, so the
- *    call stays ordered on `stream` like any other.  Calls are re-entrant as
- *    long as concurrent calls use distinct outputs and workspaces.
+ *    no device memory.  Its only state is, per device, a pool of sets of
+ *    auxiliary default-priority streams and events, and the static scratch
+ *    of wildcat_decode_noalloc.  wildcat_select splits the units into
+ *    groups, forks the groups onto one set's streams with an event recorded
+ *    on `stream`, and joins them back into `stream` before it returns, so the
+ *    call stays ordered on `stream` like any other; a call holds its set only
+ *    while it enqueues, concurrent calls take different sets (a set is
+ *    created when all are taken; sets are kept until the process ends).
+ *    Calls are re-entrant as long as concurrent calls use distinct outputs and
+ *    workspaces (wildcat_decode_noalloc: see there).
  *  - Every call only enqueues kernels on `stream` and returns; results are
  *    ready when the stream is synchronised.  A status is returned at once for
  *    argument, shape, dtype and workspace problems; those are checked on the

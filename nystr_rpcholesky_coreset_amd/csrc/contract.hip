@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "keymean.hpp"
 #include "ordered.hpp"
 #include "weights_layout.hpp"
 
@@ -867,33 +868,36 @@ __global__ __launch_bounds__(kBlock) void gather_pivots(const TK* K, const int32
   }
 }
 
-// Per-key exponent offsets for recentring: colc = -c <kbar, k_l>.
+// Per-key exponent offsets for recentring: colc = -c <kbar, k_l>.  Thread l
+// reads its key row with 16-byte loads, all issued before the fp64 dot
+// product (kbar staged in LDS).
 template <typename TK, int D>
 __global__ __launch_bounds__(kBlock) void key_offsets(const TK* K, const double* kbar, float* colc, int n, double c) {
+  constexpr int G = 16 / sizeof(TK), NG = D / G;
+  __shared__ double sk[D];
   const int u = blockIdx.y;
-  const int l = blockIdx.x * kBlock + threadIdx.x;
-  if (l >= n) return;
-  double acc = 0.0;
-  for (int e = 0; e < D; ++e) acc = fma((double)Elem<TK>::f32(K, ((size_t)u * n + l) * D + e), kbar[(size_t)u * D + e], acc);
-  colc[(size_t)u * n + l] = (float)(-c * acc);
-}
-
-// Per-unit key mean in fp64 (recentring).
-template <typename TK, int D>
-__global__ __launch_bounds__(kBlock) void key_mean(const TK* K, double* kbar, int n) {
-  __shared__ double part[kBlock];
-  const int u = blockIdx.x, t = threadIdx.x;
-  constexpr int PH = kBlock / D;
-  const int c = t % D, ph = t / D;
-  double acc = 0.0;
-  for (int l = ph; l < n; l += PH) acc += (double)Elem<TK>::f32(K, ((size_t)u * n + l) * D + c);
-  part[t] = acc;
+  for (int e = threadIdx.x; e < D; e += kBlock) sk[e] = kbar[(size_t)u * D + e];
   __syncthreads();
-  if (t < D) {
-    double s = 0.0;
-    for (int q = 0; q < PH; ++q) s += part[q * D + t];
-    kbar[(size_t)u * D + t] = s / (double)n;
+  const int l = blockIdx.x * kBlock + threadIdx.x;
+  const TK* row = K + ((size_t)u * n + min(l, n - 1)) * D;
+  uint4 raw[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) raw[g] = *reinterpret_cast<const uint4*>(row + g * G);
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint32_t w[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (G == 8) {
+        acc = fma((double)__uint_as_float(w[q] << 16), sk[g * G + 2 * q], acc);
+        acc = fma((double)__uint_as_float(w[q] & 0xFFFF0000u), sk[g * G + 2 * q + 1], acc);
+      } else {
+        acc = fma((double)__uint_as_float(w[q]), sk[g * G + q], acc);
+      }
+    }
   }
+  if (l < n) colc[(size_t)u * n + l] = (float)(-c * acc);
 }
 
 // Column min / max of V.  Workgroup (blk, u) covers rows [blk R, blk R + R),
@@ -903,13 +907,16 @@ __global__ __launch_bounds__(kBlock) void key_mean(const TK* K, double* kbar, in
 // meet in LDS, then one integer atomic min / max per column on the
 // order-encoded value (slots initialised by gather_pivots, decoded by the
 // solve's first launch).
+#ifndef WILDCAT_VR_UNR
+#define WILDCAT_VR_UNR 8   // loads in flight per thread
+#endif
 template <typename TK, int D>
 __global__ __launch_bounds__(kBlock) void value_range_part(const TK* V, int* slot, int n) {
   constexpr int G = 16 / sizeof(TK);   // elements per 16 bytes
   constexpr int NG = D / G;            // groups per row
   constexpr int RP = kBlock / NG;      // rows per pass
   constexpr int NPASS = kMinMaxRows / RP;
-  constexpr int UNR = NPASS < 8 ? NPASS : 8;
+  constexpr int UNR = NPASS < WILDCAT_VR_UNR ? NPASS : WILDCAT_VR_UNR;
   static_assert(NPASS % UNR == 0, "passes");
   __shared__ float smn[RP][D + 1], smx[RP][D + 1];
   const int u = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
@@ -1055,7 +1062,7 @@ static void launch_weights_prep(int U, int n, int r, double c, int recentre, con
   float* rowc = reinterpret_cast<float*>(w + lay.rowc);
   float* colc = reinterpret_cast<float*>(w + lay.colc);
   if (recentre) {
-    key_mean<TK, D><<<U, kBlock, 0, st>>>(Kt, kbar, n);
+    launch_key_mean<TK, D>(Kt, reinterpret_cast<double*>(w + lay.kpart), kbar, U, n, st);
     key_offsets<TK, D><<<dim3((n + kBlock - 1) / kBlock, U), kBlock, 0, st>>>(Kt, kbar, colc, n, c);
   }
   int* mm = reinterpret_cast<int*>(w + lay.mmslot);

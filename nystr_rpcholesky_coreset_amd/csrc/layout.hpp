@@ -22,10 +22,11 @@ inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 //   pivbuf [U][2][pbs]  fp64   next pivot: s, sqrt(g_s), F[s,:i], k_s (double buffered by step parity)
 //   T0     [U]          fp64   initial residual trace
 //   kbar   [U][d]       fp64   key mean (recentring only)
+//   kpart  [U][ceil(n/1024)][d] fp64  partial key sums (recentring only)
 //   stopped, reff [U] int32
 struct SelectLayout {
   int nb, npad, pbs;
-  size_t F, dres, bsum, pivbuf, T0, kbar, stopped, reff, total;
+  size_t F, dres, bsum, pivbuf, T0, kbar, kpart, stopped, reff, total;
   SelectLayout(int U, int n, int d, int r, int fbytes = 8) {
     nb = (n + kSelRowsPerBlock - 1) / kSelRowsPerBlock;
     npad = nb * kSelRowsPerBlock;
@@ -37,6 +38,7 @@ struct SelectLayout {
     pivbuf = o;  o += al256((size_t)U * 2 * pbs * 8);
     T0 = o;      o += al256((size_t)U * 8);
     kbar = o;    o += al256((size_t)U * d * 8);
+    kpart = o;   o += al256((size_t)U * ((n + 1023) / 1024) * d * 8);
     stopped = o; o += al256((size_t)U * 4);
     reff = o;    o += al256((size_t)U * 4);
     total = o;

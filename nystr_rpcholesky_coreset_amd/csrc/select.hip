@@ -35,8 +35,10 @@
 // C_l > u_i T -- the oracle's rule, up to the rounding of the sums.
 #include <climits>
 #include <mutex>
+#include <vector>
 
 #include "common.hpp"
+#include "keymean.hpp"
 #include "layout.hpp"
 
 namespace wc {
@@ -52,6 +54,7 @@ struct SelectArgs {
   double* pivbuf;       // [U][2][pbs]
   double* T0;           // [U]
   double* kbar;         // [U][D]
+  double* kpart;        // [U][mean_blocks(n)][D] partial key sums (recentring)
   int32_t* stopped;     // [U]
   int32_t* reff;        // [U]
   int n, npad, nb, r, pbs;
@@ -307,25 +310,6 @@ __global__ __launch_bounds__(kBlock) void rpc_clear(SelectArgs a, int U) {
   if (u < U) {
     a.stopped[u] = 0;
     a.reff[u] = a.r;
-  }
-}
-
-// Per-unit key mean (recentring), fp64, fixed reduction order.
-template <typename TK, int D>
-__global__ __launch_bounds__(kBlock) void rpc_kbar(SelectArgs a) {
-  __shared__ double part[kBlock];
-  const int u = blockIdx.x, t = threadIdx.x;
-  constexpr int PH = kBlock / D;   // row phases
-  const int c = t % D, ph = t / D;
-  const TK* K = reinterpret_cast<const TK*>(a.K) + (size_t)u * a.n * D;
-  double acc = 0.0;
-  for (int l = ph; l < a.n; l += PH) acc += (double)Elem<TK>::f32(K, (size_t)l * D + c);
-  part[t] = acc;
-  __syncthreads();
-  if (t < D) {
-    double s = 0.0;
-    for (int p = 0; p < PH; ++p) s += part[p * D + t];
-    a.kbar[(size_t)u * D + t] = s / (double)a.n;
   }
 }
 
@@ -591,40 +575,62 @@ constexpr int kMaxDevices = 64;
 static_assert(WILDCAT_SELECT_GROUPS >= 1 && WILDCAT_SELECT_GROUPS <= kMaxGroups, "unit groups");
 
 namespace {
+// One set of auxiliary streams (default priority, non-blocking) and the
+// events that fork them from and join them into the caller's stream.
 struct AuxStreams {
-  bool ready = false;
+  int dev = 0;
   hipStream_t s[kMaxGroups - 1] = {};
   hipEvent_t fork = nullptr, join[kMaxGroups - 1] = {};
 };
+// Per device, the sets not checked out by a call in progress.  A call takes
+// a set for the time it enqueues its work (its own streams and events, so
+// concurrent calls from several host threads do not wait for each other) and
+// returns it; sets are created when every existing one is taken and kept
+// until the process ends.
 std::mutex g_aux_mu;
-AuxStreams g_aux[kMaxDevices];
+std::vector<AuxStreams*> g_aux_free[kMaxDevices];
 
-// Auxiliary streams and events of the current device, created on first use
-// (default priority, non-blocking).  Called with g_aux_mu held.
-hipError_t aux_streams(AuxStreams** out) {
+hipError_t aux_acquire(AuxStreams** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  AuxStreams& x = g_aux[dev];
-  if (!x.ready) {
-    if ((e = hipEventCreateWithFlags(&x.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    for (int g = 0; g < kMaxGroups - 1; ++g) {
-      if ((e = hipStreamCreateWithFlags(&x.s[g], hipStreamNonBlocking)) != hipSuccess) return e;
-      if ((e = hipEventCreateWithFlags(&x.join[g], hipEventDisableTiming)) != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    if (!g_aux_free[dev].empty()) {
+      *out = g_aux_free[dev].back();
+      g_aux_free[dev].pop_back();
+      return hipSuccess;
     }
-    x.ready = true;
   }
-  *out = &x;
+  AuxStreams* x = new AuxStreams;
+  x->dev = dev;
+  if ((e = hipEventCreateWithFlags(&x->fork, hipEventDisableTiming)) != hipSuccess) return e;
+  for (int g = 0; g < kMaxGroups - 1; ++g) {
+    if ((e = hipStreamCreateWithFlags(&x->s[g], hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&x->join[g], hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = x;
   return hipSuccess;
 }
+
+// Returns a set to its device's pool (its enqueued work may still be running:
+// the next user's launches queue behind it on the same streams).
+struct AuxLease {
+  AuxStreams* x = nullptr;
+  ~AuxLease() {
+    if (x == nullptr) return;
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    g_aux_free[x->dev].push_back(x);
+  }
+};
 }  // namespace
 
 template <typename TK, int D, bool RC, typename TF>
 static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hipStream_t st) {
   const dim3 grid(a.nb, U);
   rpc_clear<<<(U + kBlock - 1) / kBlock, kBlock, 0, st>>>(a, U);
-  if (RC) rpc_kbar<TK, D><<<U, kBlock, 0, st>>>(a);
+  if (RC) launch_key_mean<TK, D>(reinterpret_cast<const TK*>(a.K), a.kpart, a.kbar, U, a.n, st);
   const size_t lds_init = (32 + 2 * D) * sizeof(double);
   const size_t lds_draw = (32 + D) * sizeof(double);
   const size_t lds_step = (32 + 2 * D + 8 * RB + a.r) * sizeof(double);
@@ -635,14 +641,14 @@ static hipError_t launch_select_t(const SelectArgs& a, int U, int32_t* r_eff, hi
   const int G = U < WILDCAT_SELECT_GROUPS ? U : WILDCAT_SELECT_GROUPS;
   const bool paired = WILDCAT_SELECT_FUSED && G >= 2 && G % 2 == 0;
   const int NS = paired ? G / 2 : G;   // streams
-  std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
   hipStream_t gs[kMaxGroups] = {st};
   SelectArgs ga[kMaxGroups];
   int gU[kMaxGroups];
+  AuxLease lease;
   AuxStreams* aux = nullptr;
   if (NS > 1) {
-    lock.lock();
-    if ((e = aux_streams(&aux)) != hipSuccess) return e;
+    if ((e = aux_acquire(&aux)) != hipSuccess) return e;
+    lease.x = aux;
     if ((e = hipEventRecord(aux->fork, st)) != hipSuccess) return e;
     for (int g = 1; g < NS; ++g) {
       gs[g] = aux->s[g - 1];
@@ -743,6 +749,7 @@ hipError_t launch_select(int bf16, int U, int n, int d, int r, double c, int rec
   a.pivbuf = reinterpret_cast<double*>(w + lay.pivbuf);
   a.T0 = reinterpret_cast<double*>(w + lay.T0);
   a.kbar = reinterpret_cast<double*>(w + lay.kbar);
+  a.kpart = reinterpret_cast<double*>(w + lay.kpart);
   a.stopped = reinterpret_cast<int32_t*>(w + lay.stopped);
   a.reff = reinterpret_cast<int32_t*>(w + lay.reff);
   a.n = n; a.npad = lay.npad; a.nb = lay.nb; a.r = r; a.pbs = lay.pbs; a.u0 = 0; a.jkeep = 0; a.c = c;

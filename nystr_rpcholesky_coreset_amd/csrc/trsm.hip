@@ -205,17 +205,21 @@ __global__ __launch_bounds__(64) void solve_inv64(SolveArgs a) {
   const int i0 = blk * 64, re = a.r_eff[u];
   const int nt = max(0, min(64, re - i0));
   const double* Lu = a.L + (size_t)u * a.r * a.r;
-  // lane j stages column j of the block: Sc[j][i] = L[i][j] (identity past r_eff)
-  for (int i = 0; i < 64; ++i) {
-    const bool in = i < nt && j < nt;
-    const double v = Lu[(size_t)min(i0 + i, a.r - 1) * a.r + min(i0 + j, a.r - 1)];
-    Sc[j * 64 + i] = in ? v : (i == j ? 1.0 : 0.0);
-  }
-  __syncthreads();
+  // lane j stages column j of the block, scaled: Sc[j][i] = L[i][j] / L[j][j]
+  // for i > j and Sc[j][j] = 1 / L[j][j] (identity past r_eff); all loads
+  // (row i: consecutive lanes, consecutive addresses) are issued before the
+  // first LDS store, and the scaling happens in registers
   {
-    const double rinv = 1.0 / Sc[j * 64 + j];
-    for (int i = j + 1; i < 64; ++i) Sc[j * 64 + i] *= rinv;
-    Sc[j * 64 + j] = rinv;
+    double v[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = Lu[(size_t)min(i0 + i, a.r - 1) * a.r + min(i0 + j, a.r - 1)];
+    const double dj = Lu[(size_t)min(i0 + j, a.r - 1) * a.r + min(i0 + j, a.r - 1)];
+    const double rinv = 1.0 / (j < nt ? dj : 1.0);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const double x = (i < nt && j < nt) ? v[i] : 0.0;   // below the diagonal only i > j is read
+      Sc[j * 64 + i] = i == j ? rinv : x * rinv;
+    }
   }
   __syncthreads();
   double b[64];

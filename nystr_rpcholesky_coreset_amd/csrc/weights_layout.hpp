@@ -41,7 +41,7 @@ struct ContractSplit {
 // padded to rp, a multiple of b), and the d+1 right-hand-side columns padded
 // to cp = 16 nct, taken nc column tiles of 16 at a time.
 #ifndef WILDCAT_SOLVE_BMAX
-#define WILDCAT_SOLVE_BMAX 512   // largest diagonal block of the solves (a power of 2, >= 64)
+#define WILDCAT_SOLVE_BMAX 256   // largest diagonal block of the solves (a power of 2, >= 64)
 #endif
 struct SolveGeom {
   int b, rp, nct, cp, nc;
@@ -59,17 +59,21 @@ struct SolveGeom {
 //   ypart   [nsplit][U][r][d+1] fp32   split-n partial contractions
 //   mmslot  [U][2][d]           int32  column min / max of V, order-encoded (atomics)
 //   kbar    [U][d]              fp64   key mean (recentring only)
+//   kpart   [U][ceil(n/1024)][d] fp64  partial key sums (recentring only)
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
 //   band    [U][rp][b]          fp64   inverses of the b x b diagonal blocks of the pivot block
 //   t1      [U][rp/2][b/2]      fp64   products of the block-inverse doubling
 //   yw, zw  [U][rp][cp]         fp64   right-hand sides during the two sweeps (yw ends as X)
-constexpr int kMinMaxRows = 512;    // rows of V per value-range workgroup
+#ifndef WILDCAT_VR_ROWS
+#define WILDCAT_VR_ROWS 512
+#endif
+constexpr int kMinMaxRows = WILDCAT_VR_ROWS;   // rows of V per value-range workgroup
 struct WeightsLayout {
   ContractSplit sp;
   SolveGeom sg;
   int nmm;                          // value-range workgroups per unit
-  size_t ypart, mmslot, kbar, rowc, colc, band, t1, yw, zw, total;
+  size_t ypart, mmslot, kbar, kpart, rowc, colc, band, t1, yw, zw, total;
   WeightsLayout(int U, int n, int d, int r, bool bf16)
       : sp(U, r, n, contract_rows_per_wg(d, r, bf16)), sg(r, d) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
@@ -77,6 +81,7 @@ struct WeightsLayout {
     ypart = o;  o += al256((size_t)sp.nsplit * U * r * (d + 1) * 4);
     mmslot = o; o += al256((size_t)U * 2 * d * 4);
     kbar = o;   o += al256((size_t)U * d * 8);
+    kpart = o;  o += al256((size_t)U * ((n + 1023) / 1024) * d * 8);
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
     band = o;   o += al256((size_t)U * sg.rp * sg.b * 8);
