@@ -119,8 +119,9 @@ def mfma_evidence(w, bins):
     try:
         for ph in ("weights", "attend"):
             us, gflop = float(f[f"{ph}_trace_us"]), float(f[f"{ph}_gflop"])
+            tflops = gflop / us * 1e3   # GFLOP per microsecond = PFLOP/s
             out[ph] = {"kernel": f[f"{ph}_kernel"], "trace_us": us, "gflop": gflop,
-                       "tflops": gflop / us * 1e-3, "frac": gflop / us * 1e-3 / MFMA_BF16_TFLOPS,
+                       "tflops": tflops, "frac": tflops / MFMA_BF16_TFLOPS,
                        "mfma_busy_frac": float(f[f"{ph}_mfma_busy_frac"])}
     except (KeyError, ValueError):
         return None
