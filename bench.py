@@ -173,14 +173,16 @@ def cpu_baseline(w, inp, bins=1, target_s=20.0, factor="f64"):
 def parity_vs_oracle(w, inp, bins, results, S_gpu, O_gpu):
     """The timed path's last outputs against the oracle units of the CPU
     baseline leg (same inputs and uniforms): pivots matched bit for bit (the
-    prefix up to the first difference, per unit or bin) and the largest
-    output error relative to max|V|."""
+    prefix up to the first difference, per unit or bin), the largest output
+    error relative to max|V|, and the oracle's smallest decision margin (how
+    close any draw came to a near tie)."""
     import numpy as np
 
     from nystr_rpcholesky_coreset_amd import inputs as I
     Vmax = float(np.abs(I.to_f64(inp["V"], w.dtype)).max())
     matched = total = 0
     err = 0.0
+    margin = float("inf")
     for uidx, ur, outs in results:
         sels = [ur.sel] if bins == 1 else [p.sel for p in ur.bins]
         for k, sel in enumerate(sels):
@@ -190,11 +192,15 @@ def parity_vs_oracle(w, inp, bins, results, S_gpu, O_gpu):
                 m += 1
             matched += m
             total += sel.r_eff
+            if sel.margins:
+                margin = min(margin, min(sel.margins))
         b = uidx // w.kv_heads
         for hq, Oo in outs.items():
             err = max(err, float(np.abs(O_gpu[b, hq].astype(np.float64) - Oo).max()) / Vmax)
     return {"units": len(results), "pivots_matched": matched, "pivots_total": total, "max_err_rel": err,
-            "tol": 2e-3 if w.dtype == "fp32" else 2e-2}
+            "tol": 2e-3 if w.dtype == "fp32" else 2e-2,
+            # smallest distance of a draw from flipping to a neighbouring index, relative to the initial trace
+            "min_decision_margin": margin}
 
 
 def main():
