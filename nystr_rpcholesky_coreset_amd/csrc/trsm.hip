@@ -5,15 +5,17 @@
 // W = h_tau(K_S, K_S)^{-1} h_tau(K_S, K); with h_tau(K_S, K_S) = L L^T from the
 // Cholesky pivot block, W [V, 1] = L^{-T} L^{-1} (h_tau(K_S, K) [V, 1]).]
 //
-// Blocked right-looking solve over diagonal blocks of b rows (b = 64 .. 512,
+// Blocked right-looking solve over diagonal blocks of b rows (b = 64 .. 256,
 // chosen from r), each block applied through its explicit inverse:
-//   inverses  the 64x64 diagonal blocks of L by substitution (one wave per
-//             block), then doubled 64 -> 128 -> .. -> b:
-//             inv([[A, 0], [B, C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]],
-//             two matrix products per level (T1 = B A^-1, then -C^-1 T1);
+//   inverses  the 64x64 diagonal blocks of L, each in one workgroup's LDS by
+//             doubling from 16x16 blocks (launched together with the sum of
+//             the split partials of Y), then doubled 64 -> 128 -> .. -> b,
+//             one launch per level:
+//             inv([[A, 0], [B, C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]]
+//             (T1 = B A^-1, then -C^-1 T1, column slab by column slab);
 //   forward   for t = 0 .. T-1:  Z_t = Dinv_t Y_t;  Y_i -= L_it Z_t (i > t);
 //   backward  for t = T-1 .. 0:  X_t = Dinv_t^T Z_t;  Z_i -= L_ti^T X_t (i < t).
-// Every step is a product of fp64 tiles: a workgroup owns 16 rows and 16 NC
+// Every sweep step is a product of fp64 tiles: a workgroup owns 16 rows and 16 NC
 // columns (NC accumulators of one MFMA each) of one product; its four waves
 // split the inner dimension into four ranges, each wave issuing all loads of
 // its range (operands straight from global memory in the MFMA lane layout)
@@ -91,7 +93,9 @@ __device__ __forceinline__ void wave_mma(const double* __restrict__ Ab, int lda,
   }
 }
 
-template <int NC> constexpr int prefetch_chunks() { return NC >= 5 ? 2 : 4; }
+// Chunks per batch of loads.  Two for NC >= 3: fewer values in flight per
+// wave, but a third wave per SIMD (measured faster than four).
+template <int NC> constexpr int prefetch_chunks() { return NC >= 3 ? 2 : 4; }
 
 // Partial sums of waves 1..3 of a workgroup, [wave - 1][c][v][lane].
 template <int NC> struct RedLds { double v[3 * NC * 4 * 64]; };
@@ -150,7 +154,6 @@ struct SolveArgs {
   const double* L;      // [U][r][r]
   const int32_t* r_eff;
   double* band;         // [U][rp][b] inverses of the diagonal blocks
-  double* T1;           // [U][rp/2][b/2] doubling scratch
   double* Y;            // [U][rp][cp] right-hand sides, then X (fp64)
   double* Z;            // [U][rp][cp]
   float* X;             // [U][r][D1] output
@@ -159,148 +162,229 @@ struct SolveArgs {
   int nsplit, U, r, rp, b, D1, cp;
 };
 
-// Y[u][i][c] = sum of the split partials in split order (fp64), 0 for rows
-// at or past r_eff and for the padding columns.  The first U d threads also
-// decode the value range of V (one launch fewer).
-__global__ __launch_bounds__(kBlock) void solve_prep(SolveArgs a) {
-  const size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x;
-  const int d = a.D1 - 1;
-  if (e < (size_t)a.U * d) {
-    const int u = (int)(e / d), c = (int)(e % d);
-    a.vmin[e] = ord_dec(a.mmslot[((size_t)u * 2) * d + c]);
-    a.vmax[e] = ord_dec(a.mmslot[((size_t)u * 2 + 1) * d + c]);
-  }
-  const size_t per = (size_t)a.rp * a.cp;
-  if (e >= per * a.U) return;
-  const int u = (int)(e / per);
-  const int i = (int)((e % per) / a.cp), c = (int)(e % a.cp);
-  const bool live = i < a.r_eff[u] && c < a.D1;
-  const size_t split = (size_t)a.U * a.r * a.D1;
-  const float* p = a.ypart + ((size_t)u * a.r + min(i, a.r - 1)) * a.D1 + min(c, a.D1 - 1);
-  double z = 0.0;
-  for (int s0 = 0; s0 < a.nsplit; s0 += 8) {   // 8 loads in flight, added in split order
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(s0 + k, a.nsplit - 1) * split];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < a.nsplit) z += (double)v[k];
-  }
-  a.Y[e] = live ? z : 0.0;
-}
+// Front of the solve, one launch with two roles:
+//  * the first U (rp / 64) workgroups invert the 64x64 diagonal blocks of L
+//    (identity past r_eff) into the band, and zero the band columns to the
+//    right of each block within its b-block;
+//  * the others form Y[u][i][c] = the sum of the split partials in split
+//    order (fp64; 0 for rows at or past r_eff and for the padding columns)
+//    and decode the value range of V.
+// Inversion of a 64x64 block, in LDS, by doubling from 16x16 blocks:
+//   16x16 diagonal blocks  substitution, lane j of wave w computing column j
+//                          of block w: x_i = (delta_ij - sum_{m<i} L_im x_m) / L_ii;
+//   16 -> 32 -> 64         inv([[A, 0], [B, C]]) = [[A^-1, 0], [-C^-1 B A^-1, C^-1]],
+//                          T1 = B A^-1 and X21 = -C^-1 T1 on v_mfma_f64_16x16x4f64.
+// The MFMA output of T1 (lane (r, q), element v = row 4v + q, column r) is
+// already the B operand of the k-step v of the next product, so within a
+// 16x16 tile T1 never leaves the registers.
+constexpr int kInvPitch = 65;   // doubles per LDS row of the staged block
 
-// Inverse of the 64x64 diagonal block `blk` of L[u] (identity past r_eff),
-// into the band; the band columns to its right in the same rows are zeroed.
-// One wave per block, lane j computes column j of the inverse by column-
-// oriented substitution from e_j: step m removes row m's value from the rows
-// below, b_i -= (L_im / L_mm) b_m (i > m), and at the end x_m = b_m / L_mm.
-// The block sits transposed and pre-scaled in LDS (Sc[m][i] = L_im / L_mm,
-// Sc[m][m] = 1 / L_mm), so step m reads the contiguous row m of Sc; those
-// reads do not depend on b and are issued one step ahead, in a batch
-// (scheduling barriers keep the batch together), and the only dependency
-// from step to step is one FMA.
-__global__ __launch_bounds__(64) void solve_inv64(SolveArgs a) {
-  __shared__ __attribute__((aligned(16))) double Sc[64 * 64];
-  const int blk = blockIdx.x, u = blockIdx.y, j = threadIdx.x;
+constexpr int kFrontLds = 2 * 64 * kInvPitch + 32 * 33;   // doubles of LDS the front launch uses
+
+__device__ __forceinline__ void invert64(const SolveArgs& a, int u, int blk, double* lds) {
+  double* const Ls = lds;
+  double* const Inv = lds + 64 * kInvPitch;
+  double* const T1s = lds + 2 * 64 * kInvPitch;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r16 = lane & 15, q = lane >> 4;
   const int i0 = blk * 64, re = a.r_eff[u];
   const int nt = max(0, min(64, re - i0));
   const double* Lu = a.L + (size_t)u * a.r * a.r;
-  // lane j stages column j of the block, scaled: Sc[j][i] = L[i][j] / L[j][j]
-  // for i > j and Sc[j][j] = 1 / L[j][j] (identity past r_eff); all loads
-  // (row i: consecutive lanes, consecutive addresses) are issued before the
-  // first LDS store, and the scaling happens in registers
   {
-    double v[64];
+    double v[16];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = Lu[(size_t)min(i0 + i, a.r - 1) * a.r + min(i0 + j, a.r - 1)];
-    const double dj = Lu[(size_t)min(i0 + j, a.r - 1) * a.r + min(i0 + j, a.r - 1)];
-    const double rinv = 1.0 / (j < nt ? dj : 1.0);
+    for (int k = 0; k < 16; ++k) {
+      const int e = t + kBlock * k, i = e >> 6, j = e & 63;
+      v[k] = (i < nt && j <= i) ? Lu[(size_t)(i0 + i) * a.r + i0 + j] : 0.0;
+    }
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const double x = (i < nt && j < nt) ? v[i] : 0.0;   // below the diagonal only i > j is read
-      Sc[j * 64 + i] = i == j ? rinv : x * rinv;
+    for (int k = 0; k < 16; ++k) {
+      const int e = t + kBlock * k, i = e >> 6, j = e & 63;
+      Ls[i * kInvPitch + j] = (i >= nt && i == j) ? 1.0 : v[k];
     }
   }
   __syncthreads();
-  double b[64];
+  // 16x16 diagonal blocks
+  if (lane < 16) {
+    const int o = 16 * wave, j = lane;
+    double x[16];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) b[i] = i == j ? 1.0 : 0.0;
-  double cur[64], nxt[64];
+    for (int i = 0; i < 16; ++i) {
+      double s = i == j ? 1.0 : 0.0;
 #pragma unroll
-  for (int i = 1; i < 64; ++i) cur[i] = Sc[i];
+      for (int m = 0; m < i; ++m) s = fma(-Ls[(o + i) * kInvPitch + o + m], x[m], s);
+      x[i] = s / Ls[(o + i) * kInvPitch + o + i];
+    }
 #pragma unroll
-  for (int m = 0; m < 63; ++m) {
-#pragma unroll
-    for (int i = m + 2; i < 64; ++i) nxt[i] = Sc[(m + 1) * 64 + i];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = m + 1; i < 64; ++i) b[i] = fma(-cur[i], b[m], b[i]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = m + 2; i < 64; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < 16; ++i) Inv[(o + i) * kInvPitch + o + j] = x[i];
   }
-  const int col0 = i0 % a.b;   // the block's columns within its b-block
+  __syncthreads();
+  // 16 -> 32: wave p takes the pair of blocks at rows 32p
+  if (wave < 2) {
+    const int o = 32 * wave;
+    f64x4 tt = {0.0, 0.0, 0.0, 0.0}, x = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      tt = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[(o + 16 + r16) * kInvPitch + o + 4 * kk + q],
+                                                Inv[(o + 4 * kk + q) * kInvPitch + o + r16], tt, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      x = __builtin_amdgcn_mfma_f64_16x16x4f64(Inv[(o + 16 + r16) * kInvPitch + o + 16 + 4 * kk + q], tt[kk], x, 0,
+                                               0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Inv[(o + 16 + 4 * v + q) * kInvPitch + o + r16] = -x[v];
+  }
+  __syncthreads();
+  // 32 -> 64: wave w owns the 16x16 tile (w / 2, w % 2) of T1 and of X21
+  {
+    const int it = wave >> 1, jt = wave & 1;
+    f64x4 tt = {0.0, 0.0, 0.0, 0.0};
+    // A^-1 lower triangular: column tile jt needs k >= 16 jt
+#pragma unroll
+    for (int kk = 4 * jt; kk < 8; ++kk)
+      tt = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[(32 + 16 * it + r16) * kInvPitch + 4 * kk + q],
+                                                Inv[(4 * kk + q) * kInvPitch + 16 * jt + r16], tt, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) T1s[(16 * it + 4 * v + q) * 33 + 16 * jt + r16] = tt[v];
+    __syncthreads();
+    f64x4 x = {0.0, 0.0, 0.0, 0.0};
+    // C^-1 lower triangular: row tile it needs k < 16 (it + 1)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      if (kk < 4 * (it + 1))
+        x = __builtin_amdgcn_mfma_f64_16x16x4f64(Inv[(32 + 16 * it + r16) * kInvPitch + 32 + 4 * kk + q],
+                                                 T1s[(4 * kk + q) * 33 + 16 * jt + r16], x, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Inv[(32 + 16 * it + 4 * v + q) * kInvPitch + 16 * jt + r16] = -x[v];
+  }
+  __syncthreads();
+  // into the band (zero above the diagonal), then the band columns to the right
+  const int col0 = i0 % a.b;
   double* Bu = a.band + ((size_t)u * a.rp + i0) * a.b;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) Bu[(size_t)i * a.b + col0 + j] = b[i] * Sc[i * 64 + i];
-  for (int i = 0; i < 64; ++i)
-    for (int c = col0 + 64 + j; c < a.b; c += 64) Bu[(size_t)i * a.b + c] = 0.0;
+  for (int k = 0; k < 16; ++k) {
+    const int e = t + kBlock * k, i = e >> 6, j = e & 63;
+    Bu[(size_t)i * a.b + col0 + j] = j <= i ? Inv[i * kInvPitch + j] : 0.0;
+  }
+  const int wr = a.b - col0 - 64;   // band columns to the right of the block in its b-block
+  for (int e = t; e < 64 * wr; e += kBlock) Bu[(size_t)(e / wr) * a.b + col0 + 64 + e % wr] = 0.0;
 }
 
-// Doubling, level s -> 2s, pair p of unit u (rows [2ps, 2ps + 2s)):
-//   T1 = B A^-1,  B = L[(2p+1)s + a][2ps + k],  A^-1 = band block at rows 2ps.
-// Workgroup tile: 16 rows x 16 NC columns of the s x s product.
-template <int NC>
-__global__ __launch_bounds__(256) void solve_dbl_t1(SolveArgs a, int s) {
-  __shared__ RedLds<NC> red;
-  const int rt = s / 16, cg = s / (16 * NC), per = rt * cg * (a.rp / (2 * s));
+__global__ __launch_bounds__(kBlock) void solve_front(SolveArgs a, int ninv, int nprep) {
+  __shared__ __attribute__((aligned(16))) double lds[kFrontLds];
+  if ((int)blockIdx.x < ninv) {
+    const int nb = a.rp / 64;
+    invert64(a, blockIdx.x / nb, blockIdx.x % nb, lds);
+    return;
+  }
+  const int d = a.D1 - 1;
+  const size_t per = (size_t)a.rp * a.cp, ny = per * a.U, step = (size_t)nprep * kBlock;
+  const size_t split = (size_t)a.U * a.r * a.D1;
+  for (size_t e = (size_t)(blockIdx.x - ninv) * kBlock + threadIdx.x; e < ny; e += step) {
+    if (e < (size_t)a.U * d) {
+      const int u = (int)(e / d), c = (int)(e % d);
+      a.vmin[e] = ord_dec(a.mmslot[((size_t)u * 2) * d + c]);
+      a.vmax[e] = ord_dec(a.mmslot[((size_t)u * 2 + 1) * d + c]);
+    }
+    const int u = (int)(e / per);
+    const int i = (int)((e % per) / a.cp), c = (int)(e % a.cp);
+    const bool live = i < a.r_eff[u] && c < a.D1;
+    const float* p = a.ypart + ((size_t)u * a.r + min(i, a.r - 1)) * a.D1 + min(c, a.D1 - 1);
+    double z = 0.0;
+    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {   // 8 loads in flight, added in split order
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(s0 + k, a.nsplit - 1) * split];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.nsplit) z += (double)v[k];
+    }
+    a.Y[e] = live ? z : 0.0;
+  }
+}
+
+// Doubling, level S -> 2S, pair p of unit u (rows [2pS, 2pS + 2S) of a
+// b-block): the lower-left block of the pair's inverse, -C^-1 B A^-1, with
+//   B = L[(2p+1)S + i][2pS + k],  A^-1, C^-1 = the band blocks at rows 2pS, (2p+1)S.
+// Its columns are independent, so a workgroup owns one slab of 16 columns
+// and the whole level is one launch.  Wave w owns row tile w of both
+// products:
+//   T1 = B A^-1[:, slab]       (S x 16; A^-1 lower triangular, so k starts
+//                               at the slab), into LDS;
+//   X21[:, slab] = -C^-1 T1    (C^-1 lower triangular: row tile w needs
+//                               k < 16 (w + 1)).
+// Every global load (the wave's rows of B and of C^-1, and its share of the
+// slab of A^-1, which goes to LDS) is issued at the start, so the launch
+// waits on memory once.
+template <int S>
+__global__ __launch_bounds__(4 * S) void solve_dbl(SolveArgs a) {
+  static_assert(S == 64 || S == 128, "levels of 64 and 128 rows");
+  constexpr int NT = 4 * S;              // threads: one wave per row tile
+  constexpr int NCH = S / 16;            // chunks of 16 k
+  constexpr int NST = (16 * S + NT - 1) / NT;
+  __shared__ double Bs[S * 16];
+  __shared__ double T1s[S * 16];
+  const int per = (a.rp / (2 * S)) * NCH;
   int u, tile;
   if (!place(blockIdx.x, per, a.U, u, tile)) return;
-  const int p = tile / (rt * cg), rem = tile % (rt * cg), ti = rem / cg, gj = rem % cg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int p = tile / NCH, c = tile % NCH;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
   const int re = a.r_eff[u];
-  const int rowA = (2 * p + 1) * s + 16 * ti;   // first row of L (and of the product, + offset)
-  const int colL = 2 * p * s;                   // column of L where B starts
-  const int c0 = 16 * NC * gj;
-  const bool live = rowA < re && colL < re;
-  const double* Lb = a.L + (size_t)u * a.r * a.r + (size_t)min(rowA, a.r - 1) * a.r + min(colL, a.r - 1);
-  const double* Ainv = a.band + ((size_t)u * a.rp + colL) * a.b + (colL % a.b) + c0;
-  f64x4 acc[NC];
-  // A^-1 is lower triangular: rows k < c0 of its column group are zero
-  wg_mma<NC, false, true>(Lb, a.r, Ainv, a.b, c0 & ~15, live ? s : 0, re - rowA, re - colL, acc, red);
-  if (wave != 0) return;
-  double* T = a.T1 + ((size_t)u * (a.rp / 2) + (size_t)p * s + 16 * ti) * (a.b / 2) + c0;
-  const int r16 = lane & 15, q = lane >> 4;
+  const int colL = 2 * p * S, rowB = (2 * p + 1) * S;
+  const int rowA = rowB + 16 * wave;
+  // B rows (zero past r_eff; indices clamped into the unit's L)
+  const double* Lu = a.L + (size_t)u * a.r * a.r;
+  const int ra = min(rowA + r16, re - 1);
+  double bl[NCH][4];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) T[(size_t)(4 * v + q) * (a.b / 2) + 16 * c + r16] = acc[c][v];
-}
-
-//   band[(2p+1)s + a][2ps - tb + c] = -(C^-1 T1)[a][c],  C^-1 = band block at rows (2p+1)s.
-template <int NC>
-__global__ __launch_bounds__(256) void solve_dbl_x21(SolveArgs a, int s) {
-  __shared__ RedLds<NC> red;
-  const int rt = s / 16, cg = s / (16 * NC), per = rt * cg * (a.rp / (2 * s));
-  int u, tile;
-  if (!place(blockIdx.x, per, a.U, u, tile)) return;
-  const int p = tile / (rt * cg), rem = tile % (rt * cg), ti = rem / cg, gj = rem % cg;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ar = 16 * ti;                       // row within C
-  const int row = (2 * p + 1) * s + ar;         // row of the band
-  const int c0 = 16 * NC * gj;
-  const double* Cinv = a.band + ((size_t)u * a.rp + row) * a.b + (((2 * p + 1) * s) % a.b);
-  const double* T = a.T1 + ((size_t)u * (a.rp / 2) + (size_t)p * s) * (a.b / 2) + c0;
-  f64x4 acc[NC];
-  // C^-1 lower triangular: rows [ar, ar + 16) need k < ar + 16
-  wg_mma<NC, false, false>(Cinv, a.b, T, a.b / 2, 0, ar + 16, 0, 0, acc, red);
-  if (wave != 0) return;
-  double* out = a.band + ((size_t)u * a.rp + row) * a.b + ((2 * p * s) % a.b) + c0;
-  const int r16 = lane & 15, q = lane >> 4;
+    for (int j = 0; j < 4; ++j) {
+      const int k = 16 * ch + 4 * q + j;
+      const bool in = ch >= c && rowA + r16 < re && colL + k < re;
+      const double v = Lu[(size_t)max(ra, 0) * a.r + max(min(colL + k, re - 1), 0)];
+      bl[ch][j] = in ? v : 0.0;
+    }
+  // C^-1 rows of the wave's row tile
+  const double* Cinv = a.band + ((size_t)u * a.rp + rowB + 16 * wave + r16) * a.b + (rowB % a.b);
+  double cx[NCH][4];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) out[(size_t)(4 * v + q) * a.b + 16 * c + r16] = -acc[c][v];
+    for (int j = 0; j < 4; ++j) cx[ch][j] = ch <= wave ? Cinv[16 * ch + 4 * q + j] : 0.0;
+  // the slab of A^-1, rows k >= 16 c
+  const double* Ainv = a.band + ((size_t)u * a.rp + colL) * a.b + (colL % a.b) + 16 * c;
+  double st[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int e = 256 * c + threadIdx.x + NT * i;
+    st[i] = e < 16 * S ? Ainv[(size_t)(e >> 4) * a.b + (e & 15)] : 0.0;
+  }
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int e = 256 * c + threadIdx.x + NT * i;
+    if (e < 16 * S) Bs[e] = st[i];
+  }
+  __syncthreads();
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    if (ch >= c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(bl[ch][j], Bs[(16 * ch + 4 * q + j) * 16 + r16], acc, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) T1s[(16 * wave + 4 * v + q) * 16 + r16] = acc[v];
+  __syncthreads();
+  acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+    if (ch <= wave)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(cx[ch][j], T1s[(16 * ch + 4 * q + j) * 16 + r16], acc, 0, 0, 0);
+  double* out = a.band + ((size_t)u * a.rp + rowB + 16 * wave) * a.b + (colL % a.b) + 16 * c;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) out[(size_t)(4 * v + q) * a.b + r16] = -acc[v];
 }
 
 // Diagonal block t of a sweep.  Forward (BWD = false): Z_t = Dinv_t Y_t.
@@ -374,6 +458,17 @@ __global__ __launch_bounds__(256) void solve_update(SolveArgs a, int t) {
   const double* Lu = a.L + (size_t)u * a.r * a.r;
   const double* Bk = (BWD ? a.Y : a.Z) + ((size_t)u * a.rp + tb) * a.cp + c0;
   const bool full = kl == a.b && i0 + 16 <= re;
+  // wave 0 reads the tile it updates before the product, so that read's
+  // latency overlaps the operand loads
+  double* C = (BWD ? a.Z : a.Y) + ((size_t)u * a.rp + i0) * a.cp + 16 * NC * gj;
+  const int r16 = lane & 15, q = lane >> 4;
+  double cur[NC][4];
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cur[c][v] = C[(size_t)(4 * v + q) * a.cp + 16 * c + r16];
+  }
   f64x4 acc[NC];
   if (!BWD) {
     const double* Ab = Lu + (size_t)min(i0, a.r - 1) * a.r + tb;
@@ -385,15 +480,10 @@ __global__ __launch_bounds__(256) void solve_update(SolveArgs a, int t) {
     else wg_mma<NC, true, true>(Ab, a.r, Bk, a.cp, 0, ke, re - i0, kl, acc, red);
   }
   if (wave != 0) return;
-  double* C = (BWD ? a.Z : a.Y) + ((size_t)u * a.rp + i0) * a.cp + c0;
-  const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      double* y = C + (size_t)(4 * v + q) * a.cp + 16 * c + r16;
-      *y -= acc[c][v];
-    }
+    for (int v = 0; v < 4; ++v) C[(size_t)(4 * v + q) * a.cp + 16 * c + r16] = cur[c][v] - acc[c][v];
 }
 
 template <int NC>
@@ -421,17 +511,18 @@ hipError_t launch_trsm(int U, int r, int d, const float* ypart, int nsplit, cons
   a.ypart = ypart; a.L = L; a.r_eff = r_eff; a.X = X;
   a.mmslot = reinterpret_cast<const int*>(ws + lay.mmslot); a.vmin = vmin; a.vmax = vmax;
   a.band = reinterpret_cast<double*>(ws + lay.band);
-  a.T1 = reinterpret_cast<double*>(ws + lay.t1);
   a.Y = reinterpret_cast<double*>(ws + lay.yw);
   a.Z = reinterpret_cast<double*>(ws + lay.zw);
   a.nsplit = nsplit; a.U = U; a.r = r; a.rp = g.rp; a.b = g.b; a.D1 = d + 1; a.cp = g.cp;
-  const size_t ny = (size_t)U * g.rp * g.cp;
-  solve_prep<<<(unsigned)((ny + kBlock - 1) / kBlock), kBlock, 0, st>>>(a);
-  solve_inv64<<<dim3(g.rp / 64, U), 64, 0, st>>>(a);
+  // front: the block inverses, and summing workgroups to make about two per
+  // CU with them (the summing role loops over Y)
+  const int ninv = U * (g.rp / 64);
+  const int nprep = ninv < 384 ? 512 - ninv : 128;
+  solve_front<<<(unsigned)(ninv + nprep), kBlock, 0, st>>>(a, ninv, nprep);
   for (int s = 64; s < g.b; s *= 2) {
-    const int pairs = g.rp / (2 * s), per = (s / 16) * (s / 64) * pairs;
-    solve_dbl_t1<4><<<grid_for(per, U), 256, 0, st>>>(a, s);
-    solve_dbl_x21<4><<<grid_for(per, U), 256, 0, st>>>(a, s);
+    const unsigned grid = grid_for((g.rp / (2 * s)) * (s / 16), U);
+    if (s == 64) solve_dbl<64><<<grid, 4 * 64, 0, st>>>(a);
+    else solve_dbl<128><<<grid, 4 * 128, 0, st>>>(a);
   }
   switch (g.nc) {
     case 2: launch_sweeps<2>(a, g, st); break;

@@ -41,8 +41,9 @@ struct ContractSplit {
 // padded to rp, a multiple of b), and the d+1 right-hand-side columns padded
 // to cp = 16 nct, taken nc column tiles of 16 at a time.
 #ifndef WILDCAT_SOLVE_BMAX
-#define WILDCAT_SOLVE_BMAX 256   // largest diagonal block of the solves (a power of 2, >= 64)
+#define WILDCAT_SOLVE_BMAX 256   // largest diagonal block of the solves (a power of 2, 64 .. 256)
 #endif
+static_assert(WILDCAT_SOLVE_BMAX >= 64 && WILDCAT_SOLVE_BMAX <= 256, "diagonal blocks of 64 .. 256 rows");
 struct SolveGeom {
   int b, rp, nct, cp, nc;
   SolveGeom(int r, int d) {
@@ -63,7 +64,6 @@ struct SolveGeom {
 //   rowc    [U][r]              fp32   per-pivot exponent offsets (recentring only)
 //   colc    [U][n]              fp32   per-key exponent offsets (recentring only)
 //   band    [U][rp][b]          fp64   inverses of the b x b diagonal blocks of the pivot block
-//   t1      [U][rp/2][b/2]      fp64   products of the block-inverse doubling
 //   yw, zw  [U][rp][cp]         fp64   right-hand sides during the two sweeps (yw ends as X)
 #ifndef WILDCAT_VR_ROWS
 #define WILDCAT_VR_ROWS 512
@@ -73,7 +73,7 @@ struct WeightsLayout {
   ContractSplit sp;
   SolveGeom sg;
   int nmm;                          // value-range workgroups per unit
-  size_t ypart, mmslot, kbar, kpart, rowc, colc, band, t1, yw, zw, total;
+  size_t ypart, mmslot, kbar, kpart, rowc, colc, band, yw, zw, total;
   WeightsLayout(int U, int n, int d, int r, bool bf16)
       : sp(U, r, n, contract_rows_per_wg(d, r, bf16)), sg(r, d) {
     nmm = (n + kMinMaxRows - 1) / kMinMaxRows;
@@ -85,7 +85,6 @@ struct WeightsLayout {
     rowc = o;   o += al256((size_t)U * r * 4);
     colc = o;   o += al256((size_t)U * n * 4);
     band = o;   o += al256((size_t)U * sg.rp * sg.b * 8);
-    t1 = o;     o += al256((size_t)U * (sg.rp / 2) * (sg.b / 2) * 8);
     yw = o;     o += al256((size_t)U * sg.rp * sg.cp * 8);
     zw = o;     o += al256((size_t)U * sg.rp * sg.cp * 8);
     total = o;
