@@ -152,6 +152,32 @@ def test_duplicated_keys_stop_at_distinct_count():
     assert rel_max(g["O"][0, 0], exact, np.abs(V).max()) < 2e-3
 
 
+@pytest.mark.parametrize("M,d", [(70, 16), (330, 16), (330, 128)])
+def test_early_stop_inside_solve_blocks(M, d):
+    """Copies of M distinct keys of one norm stop the selection at r_eff = M
+    (equal diagonals: the residual trace falls from at least half a diagonal
+    entry to rounding noise once every distinct key is a pivot, far from the
+    stop threshold on either side), while r = 600 pads the rank to three
+    256-row solve blocks: r_eff falls inside a 64-row block, so the identity
+    tail of the block inverses, the guarded doubling tiles and the partial
+    sweep tiles all take part."""
+    rng = np.random.default_rng(100 + M + d)
+    beta = 0.5
+    base = rng.standard_normal((M, d))
+    base *= np.sqrt(18.0 / beta) / np.linalg.norm(base, axis=1, keepdims=True)
+    n = 2000
+    K = base[rng.integers(0, M, n)]
+    K[:M] = base
+    V = rng.standard_normal((n, d))
+    Q = rng.standard_normal((1, 64, d)) / np.sqrt(d)
+    inp = _edge_inputs(K, V, Q, 600, beta)
+    g = _run_gpu(inp)
+    ref = oracle_units(inp, [0])[0]
+    assert ref.sel.r_eff == M
+    assert g["r_eff"][0] == M
+    _compare_unit(inp, g, 0, ref)
+
+
 @pytest.mark.parametrize("n,r", [(64, 64), (1, 1), (513, 1), (600, 600)])
 def test_rank_extremes(n, r):
     """Well-conditioned kernels (|k|^2 ~ 16, beta 1/2) so that r = n runs to
