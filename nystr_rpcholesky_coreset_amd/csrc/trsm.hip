@@ -17,10 +17,10 @@
 //   backward  for t = T-1 .. 0:  X_t = Dinv_t^T Z_t;  Z_i -= L_ti^T X_t (i < t).
 // Every sweep step is a product of fp64 tiles: a workgroup owns 16 rows and 16 NC
 // columns (NC accumulators of one MFMA each) of one product; its four waves
-// split the inner dimension into four ranges, each wave issuing all loads of
-// its range (operands straight from global memory in the MFMA lane layout)
-// before its MFMAs, and the four partial sums meet in LDS, added in wave
-// order.  Summation order per output element is fixed, so the results are
+// split the inner dimension into four ranges, each wave loading its range in
+// batches of a few 16-wide chunks (operands straight from global memory in
+// the MFMA lane layout), each batch issued before its MFMAs, and the four
+// partial sums meet in LDS, added in wave order.  Summation order per output element is fixed, so the results are
 // bitwise reproducible.  The right-hand sides are the d+1 columns of Y padded to a
 // multiple of 16 with zeros.
 //
