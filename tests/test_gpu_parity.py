@@ -48,6 +48,9 @@ SMALL_CASES = {
     "units64_kv_gqa_d128": I.scaled_workload(C4, batch=8, q_heads=16, kv_heads=8, n=1500, m=32, r=100, seed=27),
     "units72_kv_n4096_tau": I.scaled_workload(C4, batch=9, q_heads=8, kv_heads=8, n=4096, m=16, r=48, tau=1.4,
                                               seed=28),
+    # 12 units: the solve's XCD-aware grids round up to 16 units (padding
+    # workgroups), with two 256-row solve blocks (r = 300)
+    "units12_kv_r300": I.scaled_workload(C4, batch=3, q_heads=8, kv_heads=4, n=2000, m=48, r=300, seed=29),
 }
 
 
