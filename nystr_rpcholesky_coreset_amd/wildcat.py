@@ -300,9 +300,24 @@ def forward_binned(Q, K, V, u, r, bins, beta, tau=1.0, recentre=False, stream=No
     return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)
 
 
-def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None, factor="f64"):
-    """WildCat module: select -> weights -> attend on one stream.  Returns (O, parts)."""
+def compress_kv(K, V, u, r, beta, tau=1.0, recentre=True, stream=None, factor="f64"):
+    """CompressKV: wildcat_select then wildcat_weights, returning the
+    compressed cache dict(S, r_eff, L, K_S, X, vmin, vmax) that attend and
+    decode consume.
+
+    [WildCat, recentring paragraph and CompressKV / Alg. 2 paragraph: the
+    compression works on the recentred keys k - kbar, kbar the mean of the
+    unit's keys, so recentring is on unless turned off; the temperature tau
+    is the caller's, its closed form not being recoverable from the pages.]
+    Recentring never reaches attend or decode: its per-query factor cancels
+    in the ratio of the plug-in estimator, so they take the raw K_S."""
     S, r_eff, L = select(K, u, r, beta, tau, recentre, stream=stream, factor=factor)
     K_S, X, vmin, vmax = weights(K, V, S, r_eff, L, r, beta, tau, recentre, stream=stream)
-    O = attend(Q, K_S, X, vmin, vmax, beta, stream=stream)
-    return O, dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)
+    return dict(S=S, r_eff=r_eff, L=L, K_S=K_S, X=X, vmin=vmin, vmax=vmax)
+
+
+def forward(Q, K, V, u, r, beta, tau=1.0, recentre=False, stream=None, factor="f64"):
+    """WildCat module: select -> weights -> attend on one stream.  Returns (O, parts)."""
+    parts = compress_kv(K, V, u, r, beta, tau, recentre, stream=stream, factor=factor)
+    O = attend(Q, parts["K_S"], parts["X"], parts["vmin"], parts["vmax"], beta, stream=stream)
+    return O, parts

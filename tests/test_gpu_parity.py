@@ -348,3 +348,25 @@ def test_non_current_stream_with_concurrent_allocations():
     for k, v in got.items():
         np.testing.assert_array_equal(v.cpu().numpy(), ref[k], err_msg=k)
     del junk
+
+
+def test_compress_kv_recentres_by_default():
+    """compress_kv with its defaults runs CompressKV on recentred keys: its
+    cache equals that of forward(..., recentre=True) bit for bit, and both
+    match the oracle's CompressKV with recentring on."""
+    import torch
+    from nystr_rpcholesky_coreset_amd import wildcat as wc
+    w = I.scaled_workload(C4, q_heads=4, kv_heads=2, n=1500, m=40, r=100, recentre=True, tau=1.3, seed=31)
+    inp = I.make_inputs(w)
+    K = to_device(inp["K"], w.dtype)
+    V = to_device(inp["V"], w.dtype)
+    u = torch.from_numpy(inp["u"]).cuda()
+    cache = wc.compress_kv(K, V, u, w.r, w.beta, w.tau)
+    torch.cuda.synchronize()
+    g = _run_gpu(inp)   # forward with recentre=True
+    for k in ("S", "r_eff", "L", "X", "vmin", "vmax"):
+        np.testing.assert_array_equal(cache[k].cpu().numpy(), g[k])
+    np.testing.assert_array_equal(cache["K_S"].float().cpu().numpy(), g["K_S"])
+    ref = oracle_units(inp, list(range(w.units)))
+    for unit in range(w.units):
+        _compare_unit(inp, g, unit, ref[unit])
